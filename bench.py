@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Throughput of the fused forward pass of exact softmax attention on one MI355X.
+
+One step = one call of the C-ABI entry point over the whole workload (every query row of
+every (b, h)), with q/k/v already resident in device memory. Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+The metric is forward TFLOP/s with 4*B*H*N^2*d flops per call (two products of
+2*N^2*d per head, interactiveml.org "FlashAttention saves the matrix, not the quadratic
+work"), halved for causal masks. Beside it: the roofline of the kernel (average kernel
+duration from HIP events over the timed region, on the launch stream) and the fp64 CPU
+oracle timed on a bounded sample of query rows on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from exact_softmax_attention_fa_amd import inputs  # noqa: E402
+
+# MI355X published dense peaks (TFLOP/s): bf16 MFMA 2.5 PFLOP/s (256 CU x 2.4 GHz x 4096
+# flop/clock), fp32 MFMA 157.3 TFLOP/s.
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+KERNEL_SOURCES = ["exact_softmax_attention_fa_amd/csrc/fa_fwd_bf16.hip",
+                  "exact_softmax_attention_fa_amd/csrc/fa_fwd_f32.hip",
+                  "exact_softmax_attention_fa_amd/csrc/fa_internal.h"]
+
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
+# dispatch), each scaled by the factor the same counter reads for a plain copy of known size.
+# Keyed by workload; valid only for the kernel sources whose hash is stored with them.
+TRAFFIC = {}
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:  # noqa: BLE001
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(w: inputs.Workload, t: dict, rows_per_head: int) -> dict:
+    """The fp64 oracle, as it stands, on `rows_per_head` evenly spaced query rows of every
+    (b, h). Decoding the stored inputs to fp64 is done before the clock starts."""
+    import numpy as np
+    from oracle import attention as oracle
+    q, k, v = (oracle.as_fp64(t[x], w.dtype) for x in "qkv")
+    r = min(rows_per_head, w.N)
+    rows = np.unique(np.linspace(0, w.N - 1, r).round().astype(np.int64))
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.resolved_scale(), w.causal, rows=rows)
+    dt = time.perf_counter() - t0
+    keys = (rows + 1) if w.causal else np.full(len(rows), w.N)
+    flops = 4.0 * w.d * float(keys.sum()) * w.B * w.H
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} of {w.N} query rows (evenly spaced) in each of {w.B * w.H} heads, "
+                      f"fp64 numpy, {dt:.1f} s; flops counted per row as 4*d*visible keys"}
+
+
+def copy_calibration(mib: int, steps: int) -> None:
+    """A plain device-to-device copy of known size (reference for the HBM byte counters)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=8192,
+                    help="query rows per head for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB --steps times (HBM counter reference)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run the same kernel on its own heads). Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return 0
+
+    import torch
+    import exact_softmax_attention_fa_amd as fa
+
+    w = inputs.WORKLOADS[args.workload]
+    t = inputs.make(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def dev_tensor(x):
+        import numpy as np
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v = (dev_tensor(t[x]) for x in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    entry = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+    call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 w.B, w.H, w.N, w.d, w.resolved_scale(), 1 if w.causal else 0, stream.cuda_stream)
+
+    def step():
+        st = entry(*call_args)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, entry.__name__)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    tflops = w.flops / (wall / args.steps) / 1e12
+    achieved = w.flops / avg_kernel_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    kh = kernel_hash()
+    traffic = TRAFFIC.get(w.name)
+    traffic_bytes = traffic["bytes"] if traffic and traffic.get("kernel_hash") == kh else None
+
+    line = {
+        "metric": "fwd attention TFLOP/s (4BHN^2d), bf16 N=8192 d=128; % of MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": w.resolved_scale(), "inputs": w.note, "seed": w.seed},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic_bytes,
+                     "kernel_avg_us": round(avg_kernel_s * 1e6, 2),
+                     "algorithmic_flops_per_launch": w.flops,
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+                     "hbm_gbs_algorithmic": round(w.algorithmic_bytes / avg_kernel_s / 1e9, 1),
+                     "kernel_hash": kh},
+        "cpu_baseline": None,
+    }
+    if args.cpu_rows > 0:
+        line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,118 @@
+"""Fused forward pass of exact softmax attention on AMD MI355X (gfx950).
+
+Thin ctypes binding over the C-ABI library ``libfa.so`` (declared in include/fa.h).
+The binding only marshals arguments: every step of the computation runs in the HIP
+kernels. PyTorch supplies device memory and the stream.
+
+Entry points with the C names:
+  fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> status   (bf16, raw pointers)
+  fa_fwd_f32(...)                                              -> status   (fp32, raw pointers)
+  fa_status_string(status)                                     -> str
+and a tensor-level convenience:
+  fwd(q, k, v, scale=None, causal=False) -> (o, lse)
+If the library has not been built, every call raises RuntimeError; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_status_string", "fwd", "library_path", "load_library",
+           "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FaError"]
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("FA_LIBRARY", os.path.join(_PKG, "libfa.so"))
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+def load_library():
+    """Load libfa.so once; raise RuntimeError if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(build it with `python -m exact_softmax_attention_fa_amd.build`)")
+    lib = ctypes.CDLL(path)
+    argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                ctypes.c_void_p]
+    for name in ("fa_fwd", "fa_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
+    """bf16 forward on raw device pointers (ints); returns the C status code."""
+    return load_library().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
+    """fp32 forward on raw device pointers (ints); returns the C status code."""
+    return load_library().fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(status).decode()
+
+
+def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
+        return_lse: bool = True, stream=None):
+    """Attention forward on torch tensors of shape [B, H, N, d] (bf16 or float32, on the GPU).
+
+    Returns (o, lse) with o like q and lse float32 [B, H, N] (None if return_lse is False
+    and no lse buffer is given). ``scale`` defaults to 1/sqrt(d). The work is enqueued on
+    ``stream`` (default: torch's current stream) and is not waited for.
+    """
+    import torch
+
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [B,H,N,d] shape, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32
+                              or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None,
+            B, H, N, d, float(scale), 1 if causal else 0, handle)
+    if st != FA_OK:
+        raise FaError(st, fn.__name__)
+    return out, lse

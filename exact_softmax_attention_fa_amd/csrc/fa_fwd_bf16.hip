@@ -1,0 +1,395 @@
+// Fused forward pass of exact softmax attention, bf16 inputs, for gfx950 (CDNA4).
+//
+// Method (liminalml.com "FlashAttention", online update equations; interactiveml.org
+// "FlashAttention saves the matrix, not the quadratic work"): every query row keeps a
+// running maximum m, a denominator l and an unnormalised numerator u; for each block of
+// keys, m' = max(m, max s), both l and u are multiplied by e^(m - m'), and the block adds
+// p = e^(s - m') to l and p V to u. After the last block the row is u / l. Query and key
+// dimensions are both tiled and the whole computation is fused (interactiveml.org, same
+// page), so no N x N matrix leaves the chip (sadullah.online, "fused, tiled computation").
+//
+// gfx950 mapping
+// --------------
+// * One workgroup = NW waves of 64 lanes; each wave owns QW blocks of 32 query rows, so a
+//   workgroup covers BR = NW*QW*32 queries of one (b, h). Q stays in VGPRs as MFMA operands.
+// * K and V tiles of BC keys are staged in LDS, double-buffered: the global loads of tile
+//   j+1 are issued before the MFMAs of tile j and written to the other buffer afterwards.
+// * Both products use v_mfma_f32_32x32x16_bf16 with fp32 accumulation, computed transposed:
+//     S^T (keys x queries) = K Q^T      and      O^T (d x queries) += V^T P^T.
+//   In the 32x32 accumulator layout lane l holds column l%32, so every lane holds 16
+//   scores of ONE query, and in O^T every lane holds 16 output features of ONE query.
+//   Row statistics are then per-lane registers (one cross-half exchange per tile), the
+//   rescale of u is a per-lane multiply, and the probabilities go from the S^T
+//   accumulator straight into the B operand of the second product with no data movement:
+//   accumulator register i of lane l holds key 8*(i/4) + 4*(l/32) + i%4 of the 32-key
+//   block, and registers 8c..8c+7 are exactly the 8 contraction slots lane l supplies for
+//   16-key chunk c, provided the A operand (V^T) supplies the same keys in those slots.
+// * V^T operands are read from the row-major V tile with ds_read_b64_tr_b16 (a gfx950
+//   transpose read): in each group of 16 lanes, lane 4r+q points at key row r and
+//   features 4q..4q+3, and lane i receives feature i of the four rows. Two such reads give
+//   the 8 keys a lane needs.
+// * The scores are kept in base-2 units (scale * log2 e folded into one FMA before
+//   v_exp_f32). The running maximum is only raised when the new maximum exceeds it by more
+//   than 2^8 in probability terms; otherwise the stale maximum stays, probabilities may
+//   reach 2^8, and l and u stay consistent because both use the same reference. The
+//   result is the same function; only the rounding differs.
+// * Causal: key tiles past the workgroup's last query are never loaded, a wave skips the
+//   tiles past its own last query, and only tiles that straddle the diagonal are masked.
+//   Workgroups are issued heaviest first.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max rises by > 2^8
+
+// Tile configuration per padded head width: QW query blocks of 32 per wave, NW waves per
+// workgroup, BC keys per LDS tile. The defaults can be overridden at build time for sweeps.
+#ifndef FA_BF16_D64_QW
+#define FA_BF16_D64_QW 2
+#endif
+#ifndef FA_BF16_D64_NW
+#define FA_BF16_D64_NW 4
+#endif
+#ifndef FA_BF16_D64_BC
+#define FA_BF16_D64_BC 64
+#endif
+#ifndef FA_BF16_D128_QW
+#define FA_BF16_D128_QW 1
+#endif
+#ifndef FA_BF16_D128_NW
+#define FA_BF16_D128_NW 8
+#endif
+#ifndef FA_BF16_D128_BC
+#define FA_BF16_D128_BC 64
+#endif
+template <int D> struct Cfg;
+template <> struct Cfg<64>  { static constexpr int QW = FA_BF16_D64_QW, NW = FA_BF16_D64_NW, BC = FA_BF16_D64_BC; };
+template <> struct Cfg<128> { static constexpr int QW = FA_BF16_D128_QW, NW = FA_BF16_D128_NW, BC = FA_BF16_D128_BC; };
+
+__device__ __forceinline__ float pair_max(float x) {
+  // lanes l and l^32 exchange x; after the swap each lane holds both halves' values
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// 8 consecutive bf16 of one row, zero outside [0, d) (generic head width).
+__device__ __forceinline__ u32x4 load8_masked(const uint16_t* row, int col, int d) {
+  uint16_t e[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) e[t] = (col + t < d) ? row[col + t] : (uint16_t)0;
+  u32x4 r;
+  r[0] = e[0] | ((uint32_t)e[1] << 16);
+  r[1] = e[2] | ((uint32_t)e[3] << 16);
+  r[2] = e[4] | ((uint32_t)e[5] << 16);
+  r[3] = e[6] | ((uint32_t)e[7] << 16);
+  return r;
+}
+
+template <int D, bool CAUSAL, bool FULLD>
+__global__ __launch_bounds__(Cfg<D>::NW * 64, 1)
+void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int QW = Cfg<D>::QW, NW = Cfg<D>::NW, BC = Cfg<D>::BC;
+  constexpr int NT = NW * 64;
+  constexpr int BR = NW * QW * 32;
+  constexpr int KP = D + 8;    // K row pitch (elements): conflict-free 16-byte reads of 32 rows
+  constexpr int VP = D + 16;   // V row pitch: conflict-free transpose reads of 4 rows
+  constexpr int KT = BC * KP, VT = BC * VP;
+  constexpr int CH = BC * D / 8;      // 16-byte chunks per K (or V) tile
+  constexpr int CPT = CH / NT;        // chunks per thread
+  static_assert(CH % NT == 0, "tile must split evenly over the workgroup");
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shapes");
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, hh = lane >> 5;
+  const int N = a.N, d = a.d;
+
+  // Scheduler: heads vary fastest, so consecutive workgroups (which the dispatcher spreads
+  // round-robin over the 8 XCDs) keep one head on one XCD whenever B*H is a multiple of 8.
+  const int id = blockIdx.x;
+  const int qt_rev = id / a.BH;
+  const int bh = id - qt_rev * a.BH;
+  const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
+  const int q0 = qt * BR;
+
+  const size_t head = (size_t)bh * (size_t)N * (size_t)d;
+  const uint16_t* __restrict__ Qh = (const uint16_t*)a.q + head;
+  const uint16_t* __restrict__ Kh = (const uint16_t*)a.k + head;
+  const uint16_t* __restrict__ Vh = (const uint16_t*)a.v + head;
+  uint16_t* __restrict__ Oh = (uint16_t*)a.o + head;
+
+  const int wq_lo = q0 + wave * QW * 32;   // first query of this wave
+  const int wq_hi = wq_lo + QW * 32 - 1;   // last query of this wave
+
+  // Q fragments: B operand of S^T = K Q^T. Lane l supplies query l%32, features 16kk+8hh..+7.
+  u32x4 qf[QW][D / 16];
+  const uint32_t negmask = a.neg ? 0x80008000u : 0u;
+#pragma unroll
+  for (int qb = 0; qb < QW; ++qb) {
+    const int qi = wq_lo + qb * 32 + lr;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int col = 16 * kk + 8 * hh;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qi < N) {
+        if (FULLD) x = *(const u32x4*)(Qh + (size_t)qi * d + col);
+        else       x = load8_masked(Qh + (size_t)qi * d, col, d);
+      }
+      x ^= negmask;
+      qf[qb][kk] = x;
+    }
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int nkv = (kv_end + BC - 1) / BC;
+
+  f32x16 acc[QW][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < QW; ++qb)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[qb][dt][i] = 0.0f;
+  float m_run[QW], l_run[QW];
+#pragma unroll
+  for (int qb = 0; qb < QW; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.0f; }
+
+  // Global -> register staging of one K/V tile. Chunk c covers row c/(D/8), features
+  // 8*(c%(D/8))..+7; consecutive threads read consecutive 16-byte pieces of a row.
+  u32x4 kreg[CPT], vreg[CPT];
+  auto gload = [&](int j) {
+    const int key0 = j * BC;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + r * NT;
+      const int row = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      const int key = key0 + row;
+      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+      if (key < N) {
+        if (FULLD) {
+          kx = *(const u32x4*)(Kh + (size_t)key * d + col);
+          vx = *(const u32x4*)(Vh + (size_t)key * d + col);
+        } else {
+          kx = load8_masked(Kh + (size_t)key * d, col, d);
+          vx = load8_masked(Vh + (size_t)key * d, col, d);
+        }
+      }
+      kreg[r] = kx;
+      vreg[r] = vx;
+    }
+  };
+  auto swrite = [&](int buf) {
+    uint16_t* Ks = smem + buf * (KT + VT);
+    uint16_t* Vs = Ks + KT;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + r * NT;
+      const int row = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      *(u32x4*)(Ks + row * KP + col) = kreg[r];
+      *(u32x4*)(Vs + row * VP + col) = vreg[r];
+    }
+  };
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  // Lane roles in the transpose read of V: group of 16 lanes g = lane/16.
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);       // key row within a 16-key chunk (+8 for the 2nd read)
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // feature within a 32-wide block
+
+  for (int j = 0; j < nkv; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nkv) gload(j + 1);
+    const uint16_t* Ks = smem + buf * (KT + VT);
+    const uint16_t* Vs = Ks + KT;
+    const int key0 = j * BC;
+
+    if (!CAUSAL || key0 <= wq_hi) {
+      // ---- S^T = K Q^T : BC keys x 32 queries per query block -------------------------
+      f32x16 s[QW][BC / 32];
+#pragma unroll
+      for (int qb = 0; qb < QW; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[qb][kb][i] = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const u32x4 kx = *(const u32x4*)(Ks + (kb * 32 + lr) * KP + 16 * kk + 8 * hh);
+#pragma unroll
+          for (int qb = 0; qb < QW; ++qb)
+            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, kx), __builtin_bit_cast(bf16x8, qf[qb][kk]), s[qb][kb], 0, 0, 0);
+        }
+      }
+
+      // ---- online softmax update, one query per lane -----------------------------------
+      const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq_lo);
+      u32x4 pb[QW][BC / 16];   // probabilities as bf16, B operand chunks of 16 keys
+#pragma unroll
+      for (int qb = 0; qb < QW; ++qb) {
+        const int qi = wq_lo + qb * 32 + lr;
+        float mt = -INFINITY;
+        if (masked) {
+#pragma unroll
+          for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+              const bool dead = key >= N || (CAUSAL && key > qi);
+              const float t = dead ? -INFINITY : s[qb][kb][i] * a.sl2;
+              s[qb][kb][i] = t;
+              mt = fmaxf(mt, t);
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[qb][kb][i]);
+          mt *= a.sl2;
+        }
+        mt = pair_max(mt);
+        const float m_new = fmaxf(m_run[qb], mt);
+        const bool grow = m_new > m_run[qb] + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float alpha = exp2f(m_run[qb] - m_new);  // 0 while m_run is -inf
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[qb][dt][i] *= alpha;
+          m_run[qb] = m_new;
+        }
+        const float msub = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+        float lsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb) {
+          float p[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            p[i] = masked ? __builtin_amdgcn_exp2f(s[qb][kb][i] - msub)
+                          : __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], a.sl2, -msub));
+            lsum += p[i];
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            u32x4 w;
+            w[0] = pack_bf16x2(p[8 * c + 0], p[8 * c + 1]);
+            w[1] = pack_bf16x2(p[8 * c + 2], p[8 * c + 3]);
+            w[2] = pack_bf16x2(p[8 * c + 4], p[8 * c + 5]);
+            w[3] = pack_bf16x2(p[8 * c + 6], p[8 * c + 7]);
+            pb[qb][2 * kb + c] = w;
+          }
+        }
+        l_run[qb] += lsum;
+      }
+
+      // ---- O^T += V^T P^T ----------------------------------------------------------------
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int c16 = 0; c16 < BC / 16; ++c16) {
+          const uint16_t* base = Vs + (c16 * 16 + tr_row) * VP + dt * 32 + tr_col;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * VP));
+          u32x4 av;
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          av[0] = lo2[0]; av[1] = lo2[1]; av[2] = hi2[0]; av[3] = hi2[1];
+#pragma unroll
+          for (int qb = 0; qb < QW; ++qb)
+            acc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pb[qb][c16]), acc[qb][dt], 0, 0, 0);
+        }
+      }
+    }
+
+    if (j + 1 < nkv) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: o = u / l, lse = (m + log2 l) * ln 2 ----------------------------------------
+#pragma unroll
+  for (int qb = 0; qb < QW; ++qb) {
+    const int qi = wq_lo + qb * 32 + lr;
+    const float l_tot = pair_sum(l_run[qb]);
+    const float inv = 1.0f / l_tot;
+    if (qi < N) {
+      uint16_t* orow = Oh + (size_t)qi * d;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = dt * 32 + 8 * g + 4 * hh;   // 4 consecutive features
+          const float x0 = acc[qb][dt][4 * g + 0] * inv, x1 = acc[qb][dt][4 * g + 1] * inv;
+          const float x2 = acc[qb][dt][4 * g + 2] * inv, x3 = acc[qb][dt][4 * g + 3] * inv;
+          if (FULLD) {
+            u32x2 w;
+            w[0] = pack_bf16x2(x0, x1);
+            w[1] = pack_bf16x2(x2, x3);
+            *(u32x2*)(orow + col) = w;
+          } else {
+            const float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (col + t < d) orow[col + t] = __builtin_bit_cast(uint16_t, (__bf16)xs[t]);
+          }
+        }
+      if (a.lse != nullptr && hh == 0) {
+        const float msub = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+        a.lse[(size_t)bh * N + qi] = (msub + __log2f(l_tot)) * 0.69314718055994531f;
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.BH * a.n_qtiles));
+  const dim3 block(Cfg<D>::NW * 64);
+  if (fulld) hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), grid, block, 0, stream, a);
+  else       hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int bf16_rows_per_block(int d_pad) {
+  return d_pad == 64 ? Cfg<64>::NW * Cfg<64>::QW * 32 : Cfg<128>::NW * Cfg<128>::QW * 32;
+}
+
+hipError_t launch_bf16(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream) {
+  const bool fulld = (a.d == d_pad);
+  if (d_pad == 64) return causal ? launch_one<64, true>(a, fulld, stream) : launch_one<64, false>(a, fulld, stream);
+  return causal ? launch_one<128, true>(a, fulld, stream) : launch_one<128, false>(a, fulld, stream);
+}
+
+}  // namespace fa

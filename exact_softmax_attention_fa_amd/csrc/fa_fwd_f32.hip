@@ -1,0 +1,277 @@
+// Fused forward pass of exact softmax attention, fp32 inputs, for gfx950 (CDNA4).
+//
+// Same method and data flow as the bf16 kernel (online softmax over key tiles with the
+// running max, denominator and numerator rescaled together; liminalml.com
+// "FlashAttention", online update equations), with fp32 operands throughout: both
+// products use v_mfma_f32_32x32x2_f32 and the probabilities stay fp32.
+//
+// Layout (transposed products, as in the bf16 kernel):
+//   S^T = K Q^T : A operand lane l = K[key l%32][feature slot], B operand = Q[query l%32][slot]
+//   O^T += V^T P^T : the 16 accumulator registers of S^T hold keys 8*(i/4)+4*(l/32)+i%4 of
+//   one query; register i is the B operand of one MFMA whose two contraction slots are the
+//   keys of the two lane halves, and the A operand is V[that key][feature l%32], read from
+//   a row-major V tile (consecutive lanes read consecutive features).
+// The contraction over features is permuted: in MFMA step kk, lane half h supplies feature
+// kk + h*D/2, so every lane reads one contiguous run of a K row and of its Q row.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int D> struct CfgF;
+template <> struct CfgF<64>  { static constexpr int NW = 2, BC = 32; };
+template <> struct CfgF<128> { static constexpr int NW = 2, BC = 32; };
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ f32x4 load4_masked(const float* row, int col, int d) {
+  f32x4 r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) r[t] = (col + t < d) ? row[col + t] : 0.0f;
+  return r;
+}
+
+template <int D, bool CAUSAL, bool FULLD>
+__global__ __launch_bounds__(CfgF<D>::NW * 64, 1)
+void fwd_f32_kernel(FwdArgs a) {
+  constexpr int NW = CfgF<D>::NW, BC = CfgF<D>::BC;
+  constexpr int NT = NW * 64;
+  constexpr int BR = NW * 32;
+  constexpr int KP = D + 1;   // odd pitch: the 32 rows of one read fall in distinct banks
+  constexpr int VP = D + 4;
+  constexpr int KT = BC * KP, VT = BC * VP;
+  constexpr int CH = BC * D / 4;   // 16-byte chunks per tile
+  constexpr int CPT = CH / NT;
+  constexpr int H2 = D / 2;
+  static_assert(CH % NT == 0, "tile must split evenly over the workgroup");
+
+  __shared__ __attribute__((aligned(16))) float smem[2 * (KT + VT)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, hh = lane >> 5;
+  const int N = a.N, d = a.d;
+
+  const int id = blockIdx.x;
+  const int qt_rev = id / a.BH;
+  const int bh = id - qt_rev * a.BH;
+  const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
+  const int q0 = qt * BR;
+
+  const size_t head = (size_t)bh * (size_t)N * (size_t)d;
+  const float* __restrict__ Qh = (const float*)a.q + head;
+  const float* __restrict__ Kh = (const float*)a.k + head;
+  const float* __restrict__ Vh = (const float*)a.v + head;
+  float* __restrict__ Oh = (float*)a.o + head;
+
+  const int wq_lo = q0 + wave * 32;
+  const int wq_hi = wq_lo + 31;
+  const int qi = wq_lo + lr;
+
+  // Q operand: step kk uses feature kk + hh*D/2.
+  float qf[H2];
+  {
+    const float sgn = a.neg ? -1.0f : 1.0f;
+#pragma unroll
+    for (int kk = 0; kk < H2; ++kk) {
+      const int col = kk + hh * H2;
+      qf[kk] = (qi < N && col < d) ? sgn * Qh[(size_t)qi * d + col] : 0.0f;
+    }
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int nkv = (kv_end + BC - 1) / BC;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  f32x4 kreg[CPT], vreg[CPT];
+  auto gload = [&](int j) {
+    const int key0 = j * BC;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + r * NT;
+      const int row = c / (D / 4);
+      const int col = (c % (D / 4)) * 4;
+      const int key = key0 + row;
+      f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
+      if (key < N) {
+        if (FULLD) {
+          kx = *(const f32x4*)(Kh + (size_t)key * d + col);
+          vx = *(const f32x4*)(Vh + (size_t)key * d + col);
+        } else {
+          kx = load4_masked(Kh + (size_t)key * d, col, d);
+          vx = load4_masked(Vh + (size_t)key * d, col, d);
+        }
+      }
+      kreg[r] = kx;
+      vreg[r] = vx;
+    }
+  };
+  auto swrite = [&](int buf) {
+    float* Ks = smem + buf * (KT + VT);
+    float* Vs = Ks + KT;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + r * NT;
+      const int row = c / (D / 4);
+      const int col = (c % (D / 4)) * 4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Ks[row * KP + col + t] = kreg[r][t];   // odd pitch: scalar stores
+      *(f32x4*)(Vs + row * VP + col) = vreg[r];
+    }
+  };
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  for (int j = 0; j < nkv; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nkv) gload(j + 1);
+    const float* Ks = smem + buf * (KT + VT);
+    const float* Vs = Ks + KT;
+    const int key0 = j * BC;
+
+    if (!CAUSAL || key0 <= wq_hi) {
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+        const float* krow = Ks + (kb * 32 + lr) * KP + hh * H2;
+#pragma unroll
+        for (int kk = 0; kk < H2; ++kk)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[kk], qf[kk], s[kb], 0, 0, 0);
+      }
+
+      const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq_lo);
+      float mt = -INFINITY;
+      if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const bool dead = key >= N || (CAUSAL && key > qi);
+            const float t = dead ? -INFINITY : s[kb][i] * a.sl2;
+            s[kb][i] = t;
+            mt = fmaxf(mt, t);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
+        mt *= a.sl2;
+      }
+      mt = pair_max(mt);
+      const float m_new = fmaxf(m_run, mt);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThreshold)) {
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+        m_run = m_new;
+      }
+      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = masked ? __builtin_amdgcn_exp2f(s[kb][i] - msub)
+                                 : __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.sl2, -msub));
+          s[kb][i] = p;
+          lsum += p;
+        }
+      l_run += lsum;
+
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const float* vrow = Vs + key * VP + lr;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[dt * 32], s[kb][i], acc[dt], 0, 0, 0);
+        }
+    }
+
+    if (j + 1 < nkv) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = pair_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (qi < N) {
+    float* orow = Oh + (size_t)qi * d;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = dt * 32 + 8 * g + 4 * hh;
+        f32x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = acc[dt][4 * g + t] * inv;
+        if (FULLD) {
+          *(f32x4*)(orow + col) = w;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (col + t < d) orow[col + t] = w[t];
+        }
+      }
+    if (a.lse != nullptr && hh == 0) {
+      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+      a.lse[(size_t)bh * N + qi] = (msub + log2f(l_tot)) * 0.69314718055994531f;
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.BH * a.n_qtiles));
+  const dim3 block(CfgF<D>::NW * 64);
+  if (fulld) hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, true>), grid, block, 0, stream, a);
+  else       hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int f32_rows_per_block(int d_pad) {
+  return d_pad == 64 ? CfgF<64>::NW * 32 : CfgF<128>::NW * 32;
+}
+
+hipError_t launch_f32(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream) {
+  const bool fulld = (a.d == d_pad);
+  if (d_pad == 64) return causal ? launch_one<64, true>(a, fulld, stream) : launch_one<64, false>(a, fulld, stream);
+  return causal ? launch_one<128, true>(a, fulld, stream) : launch_one<128, false>(a, fulld, stream);
+}
+
+}  // namespace fa

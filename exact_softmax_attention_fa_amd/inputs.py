@@ -166,9 +166,11 @@ def scalar_case(scores, values) -> dict:
 
 def sample_rows(N: int, count: int, seed: int, tile_edges=(1, 63, 64, 127, 128, 255, 256)) -> np.ndarray:
     """Query rows for sampled parity at full size: tile edges, the middle, the last
-    row, and seeded random rows, sorted and unique."""
+    row, and seeded random rows; max(count, number of fixed rows) unique rows, sorted."""
     fixed = {0, N // 2, N - 1}
     fixed.update(t for t in tile_edges if t < N)
+    fixed = np.array(sorted(fixed), dtype=np.int64)
+    rest = np.setdiff1d(np.arange(N, dtype=np.int64), fixed)
     rng = np.random.default_rng(seed)
-    extra = rng.choice(N, size=min(N, max(0, count - len(fixed))), replace=False)
-    return np.unique(np.concatenate([np.fromiter(fixed, dtype=np.int64), extra.astype(np.int64)]))
+    extra = rng.choice(rest, size=min(len(rest), max(0, count - len(fixed))), replace=False)
+    return np.sort(np.concatenate([fixed, extra.astype(np.int64)]))

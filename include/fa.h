@@ -1,0 +1,79 @@
+/*
+ * fa.h — fused forward pass of exact dense softmax attention on AMD MI355X (gfx950).
+ *
+ * Operation (lihaoran.work, "The intermediate matrix comes first": O = softmax(QK^T/sqrt(d)) V,
+ * with N the sequence length and d the head dimension; here the score scale is a parameter):
+ *
+ *   for every batch b, head h and query row i (0 <= i < N):
+ *     s_ij      = scale * sum_c q[b,h,i,c] * k[b,h,j,c]      for j in J_i
+ *     J_i       = {0 .. N-1}, or {0 .. i} when causal = 1 (key j kept only when j <= i)
+ *     o[b,h,i,:] = sum_{j in J_i} exp(s_ij - lse_i) * v[b,h,j,:]
+ *     lse[b,h,i] = ln sum_{j in J_i} exp(s_ij)                (natural log, fp32)
+ *
+ * The library computes this in one fused, tiled pass. Each query row carries the running
+ * maximum m, the running denominator l and the unnormalised numerator u across key/value
+ * tiles, and rescales l and u together by e^(m - m') whenever the maximum rises
+ * (liminalml.com, "FlashAttention", online update equations; interactiveml.org,
+ * "FlashAttention saves the matrix, not the quadratic work", merge of three sufficient
+ * statistics). No N x N score or probability matrix is ever written to device memory
+ * (sadullah.online, "FlashAttention's trick: fused, tiled computation").
+ *
+ * Results equal the definition up to floating-point rounding, not bit for bit: the
+ * summation order differs from a materialised implementation (lihaoran.work, "Exact
+ * attention does not mean bitwise equality").
+ *
+ * Layout: q, k, v, o are contiguous row-major [B][H][N][d] arrays (d fastest); lse is a
+ * contiguous [B][H][N] fp32 array. All pointers are device pointers owned by the caller.
+ * The library allocates no device memory, keeps no state between calls and may be called
+ * from several host threads at once.
+ *
+ * Execution: work is enqueued on `stream` (NULL = the default stream) and the call returns
+ * without waiting for it. Outputs must not overlap inputs.
+ *
+ * Errors: every argument check runs on the host before any HIP call, and a rejected call
+ * writes nothing. Bad device pointers are not detected (C convention). A failed kernel
+ * launch returns FA_ERR_HIP; asynchronous faults surface on the caller's next
+ * synchronisation.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null q/k/v/o, B/H/N/d < 1, non-finite or non-positive-size problem,
+                              causal not 0/1, element count above 2^62 */
+  FA_ERR_UNSUPPORTED = -2, /* d > 128 (the largest head width compiled), or a grid too large */
+  FA_ERR_HIP = -3          /* the HIP runtime rejected the launch */
+} fa_status;
+
+/* bf16 inputs and output (the hot path).
+ *   q, k, v : device, bf16 (IEEE binary32 upper halves), [B][H][N][d], read only
+ *   o       : device, bf16 [B][H][N][d], written (round to nearest even from fp32)
+ *   lse     : device, fp32 [B][H][N], written; may be NULL to skip it
+ *   scale   : multiplies q.k before the softmax; must be finite (callers pass 1/sqrt(d))
+ *   causal  : 0 = all keys, 1 = keys j <= i
+ * Arithmetic: fp32 accumulation of both products; the probabilities are rounded to bf16
+ * before the product with V; statistics and the normalisation are fp32.
+ * Supported: 1 <= d <= 128 (d = 64 and d = 128 are the tuned widths), any N >= 1. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* fp32 inputs and output; same parameters and semantics as fa_fwd. Both products use
+ * fp32 matrix instructions with fp32 accumulation; the probabilities stay fp32. */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,78 @@
+"""Shared helpers of the GPU parity tests: move stored inputs to the device, run the HIP
+path through the C-ABI binding, compare with the oracle at the stated tolerances."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+from exact_softmax_attention_fa_amd import inputs
+from oracle import attention as oracle
+
+# Tolerances (stated for the method): fp32 inputs max abs 1e-5; bf16 inputs with fp32
+# accumulation max abs 2e-2 and mean abs 5e-3; log-normaliser max abs 1e-3.
+TOL = {"f32": {"max": 1e-5, "mean": 1e-5, "lse": 1e-3},
+       "bf16": {"max": 2e-2, "mean": 5e-3, "lse": 1e-3}}
+
+
+def note(msg: str) -> None:
+    """Name the case before each GPU step, flushed, so a crash still says what ran."""
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def to_device(x: np.ndarray, dtype: str):
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.cuda()
+
+
+def run_gpu(t: dict, dtype: str, scale: float, causal: bool, lse=True):
+    """Inputs dict of stored arrays -> (o float64 numpy, lse float64 numpy or None)."""
+    import torch
+    import exact_softmax_attention_fa_amd as fa
+    q, k, v = (to_device(t[x], dtype) for x in "qkv")
+    o, l = fa.fwd(q, k, v, scale=scale, causal=causal, return_lse=lse)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), (l.double().cpu().numpy() if l is not None else None)
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, label: str = ""):
+    tol = TOL[dtype]
+    err = np.abs(o_gpu - o_ref)
+    stats = {"max": float(err.max()), "mean": float(err.mean())}
+    if lse_gpu is not None:
+        stats["lse"] = float(np.abs(lse_gpu - lse_ref).max())
+    assert np.all(np.isfinite(o_gpu)), f"{label}: non-finite output"
+    assert stats["max"] <= tol["max"], f"{label}: max abs error {stats['max']:.3e} > {tol['max']}"
+    assert stats["mean"] <= tol["mean"], f"{label}: mean abs error {stats['mean']:.3e} > {tol['mean']}"
+    if lse_gpu is not None:
+        assert stats["lse"] <= tol["lse"], f"{label}: lse error {stats['lse']:.3e} > {tol['lse']}"
+    return stats
+
+
+def full_parity(t: dict, dtype: str, scale: float, causal: bool, label: str):
+    note(f"full parity {label}")
+    o, l = run_gpu(t, dtype, scale, causal)
+    o_ref, l_ref = oracle.attention_stored(t["q"], t["k"], t["v"], dtype, scale, causal)
+    return compare(o, l, o_ref, l_ref, dtype, label)
+
+
+def sampled_parity(w: inputs.Workload, rows_per_head: int, label: str):
+    """Full-size workload on the GPU, oracle on sampled query rows of every (b, h)."""
+    note(f"sampled parity {label}: {w.name}")
+    t = inputs.make(w)
+    o, l = run_gpu(t, w.dtype, w.resolved_scale(), w.causal)
+    rows = np.stack([np.stack([inputs.sample_rows(w.N, rows_per_head, seed=w.seed * 100 + b * w.H + h)[:rows_per_head]
+                               for h in range(w.H)]) for b in range(w.B)])
+    o_ref, l_ref = oracle.attention_stored(t["q"], t["k"], t["v"], w.dtype, w.resolved_scale(), w.causal, rows=rows)
+    idx_b = np.arange(w.B)[:, None, None]
+    idx_h = np.arange(w.H)[None, :, None]
+    return compare(o[idx_b, idx_h, rows], l[idx_b, idx_h, rows], o_ref, l_ref, w.dtype, label)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,126 @@
+"""HIP path against the fp64 oracle, element by element, on seeded inputs.
+
+Small and medium sizes are compared in full (they span several query and key tiles and
+ragged tails); the full-size workloads are compared on sampled query rows of every
+(b, h) that the oracle computes one by one."""
+import math
+
+import numpy as np
+import pytest
+
+from exact_softmax_attention_fa_amd import inputs
+from gpu_util import TOL, compare, full_parity, note, run_gpu, sampled_parity
+from oracle import attention as oracle
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+
+
+# ---- the five workloads -------------------------------------------------------------------
+
+def test_fp32_single_head_full():
+    w = W["fwd_f32_b1_h1_n256_d64"]
+    full_parity(inputs.make(w), w.dtype, w.resolved_scale(), w.causal, w.name)
+
+
+def test_bf16_b2_h8_n1024_full():
+    w = W["fwd_bf16_b2_h8_n1024_d64"]
+    full_parity(inputs.make(w), w.dtype, w.resolved_scale(), w.causal, w.name)
+
+
+@pytest.mark.parametrize("name,rows", [
+    ("fwd_bf16_b4_h16_n4096_d128_causal", 24),
+    ("fwd_bf16_b1_h16_n8192_d128_widek", 64),
+    ("fwd_bf16_b1_h8_n32768_d128_causal", 96),
+])
+def test_full_size_sampled_rows(name, rows):
+    sampled_parity(W[name], rows, name)
+
+
+def test_widek_small_full():
+    """The boosted-key construction at a size the oracle covers in full (several tiles)."""
+    w = inputs.Workload("widek_small", 1, 4, 1100, 128, "bf16", False, 2004,
+                        k_std=3.0, boost_frac=0.01, boost_logit=8.0)
+    full_parity(inputs.make(w), "bf16", w.resolved_scale(), False, w.name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_causal_medium_full(causal):
+    t = inputs.make_random(1, 3, 777, 128, "bf16", seed=31)
+    full_parity(t, "bf16", 1 / math.sqrt(128), causal, f"n777 causal={causal}")
+
+
+# ---- scalar examples through fp32 (d = 1, scale = 1) ----------------------------------------
+
+def test_scalar_three_scores():
+    t = inputs.scalar_case([0, 1, 2], [10, 20, 30])
+    note("scalar three scores")
+    o, l = run_gpu(t, "f32", 1.0, False)
+    assert np.all(np.abs(o[0, 0, :, 0] - 25.752104) <= 1e-5), o.ravel()
+    assert np.all(np.abs(l[0, 0] - math.log(1 + math.e + math.e ** 2)) <= 1e-5)
+
+
+def test_scalar_shift_by_1000():
+    t = inputs.scalar_case([1000, 1001, 1002], [10, 20, 30])
+    note("scalar shift")
+    o, l = run_gpu(t, "f32", 1.0, False)
+    assert np.all(np.abs(o[0, 0, :, 0] - 25.752104) <= 1e-5), o.ravel()
+    assert np.all(np.abs(l[0, 0] - (1000 + math.log(1 + math.e + math.e ** 2))) <= 1e-3)
+
+
+def test_scalar_block_example():
+    t = inputs.scalar_case([1, 2, 1001, 1002], [2, -1, 4, 8])
+    note("scalar block example")
+    o, l = run_gpu(t, "f32", 1.0, False)
+    closed = (4 * math.exp(-1) + 8) / (math.exp(-1) + 1)
+    assert np.all(np.abs(o[0, 0, :, 0] - closed) <= 1e-5), o.ravel()
+    assert np.all(np.abs(l[0, 0] - (1002 + math.log(1 + math.exp(-1)))) <= 1e-3)
+
+
+def test_scalar_causal_prefixes():
+    """Causal on the block example: row i is the softmax-weighted sum of the first i+1 items."""
+    s, v = [1, 2, 1001, 1002], [2, -1, 4, 8]
+    t = inputs.scalar_case(s, v)
+    note("scalar causal prefixes")
+    o, _ = run_gpu(t, "f32", 1.0, True)
+    from oracle import online
+    for i in range(4):
+        assert abs(o[0, 0, i, 0] - online.online_scalar(s[:i + 1], v[:i + 1])) <= 1e-5
+
+
+# ---- shapes, tails and head widths ------------------------------------------------------------
+
+SHAPES = [(1, 1, 1), (1, 2, 3), (2, 1, 63), (1, 2, 64), (1, 1, 65), (1, 2, 127), (1, 1, 129),
+          (1, 1, 255), (2, 2, 257), (1, 1, 1000)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_shapes(B, H, N, d, causal):
+    t = inputs.make_random(B, H, N, d, "bf16", seed=B * 1000 + H * 100 + N + d)
+    full_parity(t, "bf16", 1 / math.sqrt(d), causal, f"bf16 B{B} H{H} N{N} d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [1, 8, 17, 40, 72, 96, 120])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_other_head_widths(d, causal):
+    t = inputs.make_random(1, 2, 200, d, "bf16", seed=500 + d)
+    full_parity(t, "bf16", 1 / math.sqrt(d), causal, f"bf16 d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [1, 3, 33, 64, 100, 128])
+@pytest.mark.parametrize("N", [1, 5, 64, 97, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_shapes(N, d, causal):
+    t = inputs.make_random(1, 2, N, d, "f32", seed=700 + N + d)
+    full_parity(t, "f32", 1 / math.sqrt(d), causal, f"f32 N{N} d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+def test_other_scales(dtype, scale):
+    t = inputs.make_random(1, 2, 150, 64, dtype, seed=901)
+    full_parity(t, dtype, scale, False, f"{dtype} scale={scale}")
+    full_parity(t, dtype, scale, True, f"{dtype} scale={scale} causal")
