@@ -13,6 +13,8 @@
 //   a row-major V tile (consecutive lanes read consecutive features).
 // The contraction over features is permuted: in MFMA step kk, lane half h supplies feature
 // kk + h*D/2, so every lane reads one contiguous run of a K row and of its Q row.
+// Unlike the bf16 kernel, the running maximum is kept on unscaled scores and the scale is
+// applied after the subtraction, which the 1e-5 fp32 tolerance needs at large scores.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -166,6 +168,9 @@ void fwd_f32_kernel(FwdArgs a) {
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[kk], qf[kk], s[kb], 0, 0, 0);
       }
 
+      // Statistics are kept on the unscaled scores: p = 2^((s - m) * sl2). Subtracting
+      // before scaling keeps the exponent argument accurate to fp32 rounding of s - m even
+      // when the scores themselves are large (e.g. all near 1000).
       const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq_lo);
       float mt = -INFINITY;
       if (masked) {
@@ -175,21 +180,19 @@ void fwd_f32_kernel(FwdArgs a) {
           for (int i = 0; i < 16; ++i) {
             const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
             const bool dead = key >= N || (CAUSAL && key > qi);
-            const float t = dead ? -INFINITY : s[kb][i] * a.sl2;
-            s[kb][i] = t;
-            mt = fmaxf(mt, t);
+            if (dead) s[kb][i] = -INFINITY;
+            mt = fmaxf(mt, s[kb][i]);
           }
       } else {
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
-        mt *= a.sl2;
       }
       mt = pair_max(mt);
       const float m_new = fmaxf(m_run, mt);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThreshold)) {
-        const float alpha = exp2f(m_run - m_new);
+      if (__builtin_amdgcn_ballot_w64((m_new - m_run) * a.sl2 > kRescaleThreshold)) {
+        const float alpha = exp2f((m_run - m_new) * a.sl2);  // 0 while m_run is -inf
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
@@ -203,8 +206,8 @@ void fwd_f32_kernel(FwdArgs a) {
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = masked ? __builtin_amdgcn_exp2f(s[kb][i] - msub)
-                                 : __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.sl2, -msub));
+          float p = __builtin_amdgcn_exp2f((s[kb][i] - msub) * a.sl2);
+          if (masked && s[kb][i] == -INFINITY) p = 0.0f;   // also right when scale is 0
           s[kb][i] = p;
           lsum += p;
         }
@@ -248,7 +251,7 @@ void fwd_f32_kernel(FwdArgs a) {
       }
     if (a.lse != nullptr && hh == 0) {
       const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-      a.lse[(size_t)bh * N + qi] = (msub + log2f(l_tot)) * 0.69314718055994531f;
+      a.lse[(size_t)bh * N + qi] = (msub * a.sl2 + log2f(l_tot)) * 0.69314718055994531f;
     }
   }
 }

@@ -9,8 +9,7 @@ import numpy as np
 import pytest
 
 from exact_softmax_attention_fa_amd import inputs
-from gpu_util import TOL, compare, full_parity, note, run_gpu, sampled_parity
-from oracle import attention as oracle
+from gpu_util import fp32_logit_bound, full_parity, note, run_gpu, sampled_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -121,6 +120,10 @@ def test_f32_shapes(N, d, causal):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
 def test_other_scales(dtype, scale):
+    """Negative, zero and large scales. At |scale| = 2.5 with d = 64 the logits are 20x
+    larger than the workloads', so the fp32 bound is derived from fp32 rounding of the dot
+    products instead of the fixed 1e-5 (which holds at scale = 1/sqrt(d))."""
     t = inputs.make_random(1, 2, 150, 64, dtype, seed=901)
-    full_parity(t, dtype, scale, False, f"{dtype} scale={scale}")
-    full_parity(t, dtype, scale, True, f"{dtype} scale={scale} causal")
+    tol = fp32_logit_bound(t, scale) if (dtype == "f32" and abs(scale) > 1.0) else None
+    full_parity(t, dtype, scale, False, f"{dtype} scale={scale}", tol)
+    full_parity(t, dtype, scale, True, f"{dtype} scale={scale} causal", tol)
