@@ -32,6 +32,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
 KERNEL_SOURCES = ["exact_softmax_attention_fa_amd/csrc/fa_fwd_bf16.hip",
+                  "exact_softmax_attention_fa_amd/csrc/fa_fwd_bf16_d128.hip",
                   "exact_softmax_attention_fa_amd/csrc/fa_fwd_f32.hip",
                   "exact_softmax_attention_fa_amd/csrc/fa_internal.h"]
 

@@ -1,5 +1,6 @@
 // C-ABI front end: argument validation, kernel selection and launch (declared in fa.h).
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <limits.h>
 #include <math.h>
 #include <stdint.h>
@@ -13,7 +14,7 @@ namespace {
 // nothing. On success fills `args` and the padded head width.
 int validate(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int N, int d, float scale, int causal, size_t elem,
-             int rows_per_block_64, int rows_per_block_128, fa::FwdArgs* args, int* d_pad) {
+             int (*rows_per_block)(int), fa::FwdArgs* args, int* d_pad) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -40,7 +41,7 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
   if (lse != nullptr && overlap(lse, lse_bytes, o, bytes)) return FA_ERR_INVALID_ARG;
 
   const int dp = d <= 64 ? 64 : 128;
-  const int br = dp == 64 ? rows_per_block_64 : rows_per_block_128;
+  const int br = rows_per_block(d);
   const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
   if ((int64_t)B * H * n_qtiles > INT_MAX) return FA_ERR_UNSUPPORTED;
 
@@ -53,7 +54,9 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
   args->d = d;
   args->BH = B * H;
   args->n_qtiles = (int)n_qtiles;
-  args->sl2 = fabsf(scale) * 1.4426950408889634f;
+  // |scale| * log2(e), floored at the smallest normal float so that a zero scale still
+  // keeps -inf (masked) scores at -inf after scaling; the floor changes no finite result.
+  args->sl2 = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
   args->neg = scale < 0.0f ? 1 : 0;
   *d_pad = dp;
   return FA_OK;
@@ -66,7 +69,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   fa::FwdArgs args;
   int d_pad = 0;
   const int st = validate(q, k, v, o, lse, B, H, N, d, scale, causal, 2,
-                          fa::bf16_rows_per_block(64), fa::bf16_rows_per_block(128), &args, &d_pad);
+                          fa::bf16_rows_per_block, &args, &d_pad);
   if (st != FA_OK) return st;
   return fa::launch_bf16(args, d_pad, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -76,7 +79,7 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
   fa::FwdArgs args;
   int d_pad = 0;
   const int st = validate(q, k, v, o, lse, B, H, N, d, scale, causal, 4,
-                          fa::f32_rows_per_block(64), fa::f32_rows_per_block(128), &args, &d_pad);
+                          fa::f32_rows_per_block, &args, &d_pad);
   if (st != FA_OK) return st;
   return fa::launch_f32(args, d_pad, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -51,6 +51,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max rises by > 2^8
@@ -75,9 +77,20 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max r
 #ifndef FA_BF16_D128_BC
 #define FA_BF16_D128_BC 64
 #endif
+// minimum waves per SIMD the register allocation must allow (1: up to 512 registers)
+#ifndef FA_BF16_D64_WPE
+#define FA_BF16_D64_WPE 1
+#endif
+#ifndef FA_BF16_D128_WPE
+#define FA_BF16_D128_WPE 2
+#endif
 template <int D> struct Cfg;
-template <> struct Cfg<64>  { static constexpr int QW = FA_BF16_D64_QW, NW = FA_BF16_D64_NW, BC = FA_BF16_D64_BC; };
-template <> struct Cfg<128> { static constexpr int QW = FA_BF16_D128_QW, NW = FA_BF16_D128_NW, BC = FA_BF16_D128_BC; };
+template <> struct Cfg<64> {
+  static constexpr int QW = FA_BF16_D64_QW, NW = FA_BF16_D64_NW, BC = FA_BF16_D64_BC, WPE = FA_BF16_D64_WPE;
+};
+template <> struct Cfg<128> {
+  static constexpr int QW = FA_BF16_D128_QW, NW = FA_BF16_D128_NW, BC = FA_BF16_D128_BC, WPE = FA_BF16_D128_WPE;
+};
 
 __device__ __forceinline__ float pair_max(float x) {
   // lanes l and l^32 exchange x; after the swap each lane holds both halves' values
@@ -90,8 +103,9 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even (v_cvt_pk_bf16_f32)
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  // one v_cvt_pk_bf16_f32: both halves rounded to nearest even
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
 // 8 consecutive bf16 of one row, zero outside [0, d) (generic head width).
@@ -107,8 +121,120 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t* row, int col, int 
   return r;
 }
 
+// Everything one wave does with one K/V tile in LDS: S^T = K Q^T, the online-softmax
+// update of its QW query blocks, and O^T += V^T P^T. MASKED selects the slower path that
+// hides keys >= N and, when causal, keys past each query.
+template <int D, int QW, int BC, int KP, int VP, bool MASKED, bool CAUSAL>
+__device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
+                                          const u32x4 (&qf)[QW][D / 16], f32x16 (&acc)[QW][D / 32],
+                                          float (&m_run)[QW], float (&l_run)[QW],
+                                          int key0, int N, int wq_lo, float sl2, int lr, int hh,
+                                          int tr_row, int tr_col) {
+  // ---- S^T = K Q^T : per 32-key block, all K operands are read before the MFMA chain ----
+  f32x16 s[QW][BC / 32];
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb) {
+    u32x4 kop[D / 16];
+    const uint16_t* krow = Ks + (kb * 32 + lr) * KP + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) kop[kk] = *(const u32x4*)(krow + 16 * kk);
+#pragma unroll
+    for (int qb = 0; qb < QW; ++qb) {
+      f32x16 c = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kop[kk]),
+                                                    __builtin_bit_cast(bf16x8, qf[qb][kk]), c, 0, 0, 0);
+      s[qb][kb] = c;
+    }
+  }
+
+  // ---- online softmax update, one query per lane ----------------------------------------
+  u32x4 pb[QW][BC / 16];   // probabilities as bf16: the B operand chunks of 16 keys
+#pragma unroll
+  for (int qb = 0; qb < QW; ++qb) {
+    const int qi = wq_lo + qb * 32 + lr;
+    float mt;
+    if (MASKED) {
+      mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const bool dead = key >= N || (CAUSAL && key > qi);
+          const float t = dead ? -INFINITY : s[qb][kb][i] * sl2;
+          s[qb][kb][i] = t;
+          mt = fmaxf(mt, t);
+        }
+    } else {
+      float m0 = s[qb][0][0], m1 = s[qb][0][1];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2) {
+          m0 = fmaxf(m0, s[qb][kb][i]);
+          m1 = fmaxf(m1, s[qb][kb][i + 1]);
+        }
+      mt = fmaxf(m0, m1) * sl2;
+    }
+    mt = pair_max(mt);
+    const float m_new = fmaxf(m_run[qb], mt);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run[qb] + kRescaleThreshold)) {
+      const float alpha = exp2f(m_run[qb] - m_new);  // 0 while m_run is -inf
+      l_run[qb] *= alpha;
+      // In-place multiply: tying each output to its input register keeps the compiler from
+      // copying the whole accumulator to merge the taken and not-taken paths.
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm("v_mul_f32 %0, %0, %1" : "+v"(acc[qb][dt][i]) : "v"(alpha));
+      m_run[qb] = m_new;
+    }
+    const float msub = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = MASKED ? __builtin_amdgcn_exp2f(s[qb][kb][i] - msub)
+                      : __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], sl2, -msub));
+        ls[i & 3] += p[i];
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        u32x4 w;
+        w[0] = pack_bf16x2(p[8 * c + 0], p[8 * c + 1]);
+        w[1] = pack_bf16x2(p[8 * c + 2], p[8 * c + 3]);
+        w[2] = pack_bf16x2(p[8 * c + 4], p[8 * c + 5]);
+        w[3] = pack_bf16x2(p[8 * c + 6], p[8 * c + 7]);
+        pb[qb][2 * kb + c] = w;
+      }
+    }
+    l_run[qb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  }
+
+  // ---- O^T += V^T P^T --------------------------------------------------------------------
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int c16 = 0; c16 < BC / 16; ++c16) {
+      const uint16_t* base = Vs + (c16 * 16 + tr_row) * VP + dt * 32 + tr_col;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * VP));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
+#pragma unroll
+      for (int qb = 0; qb < QW; ++qb)
+        acc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pb[qb][c16]), acc[qb][dt], 0, 0, 0);
+    }
+  }
+}
+
 template <int D, bool CAUSAL, bool FULLD>
-__global__ __launch_bounds__(Cfg<D>::NW * 64, 1)
+__global__ __launch_bounds__(Cfg<D>::NW * 64, Cfg<D>::WPE)
 void fwd_bf16_kernel(FwdArgs a) {
   constexpr int QW = Cfg<D>::QW, NW = Cfg<D>::NW, BC = Cfg<D>::BC;
   constexpr int NT = NW * 64;
@@ -183,24 +309,25 @@ void fwd_bf16_kernel(FwdArgs a) {
   u32x4 kreg[CPT], vreg[CPT];
   auto gload = [&](int j) {
     const int key0 = j * BC;
+    const bool whole = FULLD && key0 + BC <= N;   // no bounds checks needed for this tile
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + r * NT;
       const int row = c / (D / 8);
       const int col = (c % (D / 8)) * 8;
       const int key = key0 + row;
-      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (key < N) {
-        if (FULLD) {
-          kx = *(const u32x4*)(Kh + (size_t)key * d + col);
-          vx = *(const u32x4*)(Vh + (size_t)key * d + col);
-        } else {
+      if (whole) {
+        kreg[r] = *(const u32x4*)(Kh + (size_t)key * d + col);
+        vreg[r] = *(const u32x4*)(Vh + (size_t)key * d + col);
+      } else {
+        u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+        if (key < N) {
           kx = load8_masked(Kh + (size_t)key * d, col, d);
           vx = load8_masked(Vh + (size_t)key * d, col, d);
         }
+        kreg[r] = kx;
+        vreg[r] = vx;
       }
-      kreg[r] = kx;
-      vreg[r] = vx;
     }
   };
   auto swrite = [&](int buf) {
@@ -220,118 +347,33 @@ void fwd_bf16_kernel(FwdArgs a) {
   swrite(0);
   __syncthreads();
 
-  // Lane roles in the transpose read of V: group of 16 lanes g = lane/16.
-  const int tr_row = 4 * hh + ((lane & 15) >> 2);       // key row within a 16-key chunk (+8 for the 2nd read)
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // feature within a 32-wide block
+  // Lane roles in the transpose read of V: in each group of 16 lanes, lane 4r+q points at
+  // key row r (second read: r+8) and features 4q..4q+3 of a 16-wide half of a 32-block.
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  for (int j = 0; j < nkv; ++j) {
+  // Tiles [0, j_split) hold only keys that every query of the workgroup may see, so they
+  // take the unmasked path with no per-tile decision; the remaining tiles (the causal
+  // diagonal, or the ragged last tile) take the masked path, and under a causal mask a wave
+  // skips the tiles that lie entirely past its own last query.
+  const int j_split = CAUSAL ? min(N / BC, (q0 + 1) / BC) : N / BC;
+  int j = 0;
+  for (; j < j_split; ++j) {
     const int buf = j & 1;
     if (j + 1 < nkv) gload(j + 1);
     const uint16_t* Ks = smem + buf * (KT + VT);
-    const uint16_t* Vs = Ks + KT;
-    const int key0 = j * BC;
-
-    if (!CAUSAL || key0 <= wq_hi) {
-      // ---- S^T = K Q^T : BC keys x 32 queries per query block -------------------------
-      f32x16 s[QW][BC / 32];
-#pragma unroll
-      for (int qb = 0; qb < QW; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[qb][kb][i] = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const u32x4 kx = *(const u32x4*)(Ks + (kb * 32 + lr) * KP + 16 * kk + 8 * hh);
-#pragma unroll
-          for (int qb = 0; qb < QW; ++qb)
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, kx), __builtin_bit_cast(bf16x8, qf[qb][kk]), s[qb][kb], 0, 0, 0);
-        }
-      }
-
-      // ---- online softmax update, one query per lane -----------------------------------
-      const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq_lo);
-      u32x4 pb[QW][BC / 16];   // probabilities as bf16, B operand chunks of 16 keys
-#pragma unroll
-      for (int qb = 0; qb < QW; ++qb) {
-        const int qi = wq_lo + qb * 32 + lr;
-        float mt = -INFINITY;
-        if (masked) {
-#pragma unroll
-          for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-              const bool dead = key >= N || (CAUSAL && key > qi);
-              const float t = dead ? -INFINITY : s[qb][kb][i] * a.sl2;
-              s[qb][kb][i] = t;
-              mt = fmaxf(mt, t);
-            }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[qb][kb][i]);
-          mt *= a.sl2;
-        }
-        mt = pair_max(mt);
-        const float m_new = fmaxf(m_run[qb], mt);
-        const bool grow = m_new > m_run[qb] + kRescaleThreshold;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          const float alpha = exp2f(m_run[qb] - m_new);  // 0 while m_run is -inf
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[qb][dt][i] *= alpha;
-          m_run[qb] = m_new;
-        }
-        const float msub = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-        float lsum = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) {
-          float p[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            p[i] = masked ? __builtin_amdgcn_exp2f(s[qb][kb][i] - msub)
-                          : __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], a.sl2, -msub));
-            lsum += p[i];
-          }
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            u32x4 w;
-            w[0] = pack_bf16x2(p[8 * c + 0], p[8 * c + 1]);
-            w[1] = pack_bf16x2(p[8 * c + 2], p[8 * c + 3]);
-            w[2] = pack_bf16x2(p[8 * c + 4], p[8 * c + 5]);
-            w[3] = pack_bf16x2(p[8 * c + 6], p[8 * c + 7]);
-            pb[qb][2 * kb + c] = w;
-          }
-        }
-        l_run[qb] += lsum;
-      }
-
-      // ---- O^T += V^T P^T ----------------------------------------------------------------
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int c16 = 0; c16 < BC / 16; ++c16) {
-          const uint16_t* base = Vs + (c16 * 16 + tr_row) * VP + dt * 32 + tr_col;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * VP));
-          u32x4 av;
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          av[0] = lo2[0]; av[1] = lo2[1]; av[2] = hi2[0]; av[3] = hi2[1];
-#pragma unroll
-          for (int qb = 0; qb < QW; ++qb)
-            acc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pb[qb][c16]), acc[qb][dt], 0, 0, 0);
-        }
-      }
-    }
-
+    tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, j * BC, N, wq_lo, a.sl2,
+                                               lr, hh, tr_row, tr_col);
+    if (j + 1 < nkv) swrite(buf ^ 1);
+    __syncthreads();
+  }
+  for (; j < nkv; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nkv) gload(j + 1);
+    const uint16_t* Ks = smem + buf * (KT + VT);
+    if (!CAUSAL || j * BC <= wq_hi)
+      tile_step<D, QW, BC, KP, VP, true, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, j * BC, N, wq_lo, a.sl2,
+                                                lr, hh, tr_row, tr_col);
     if (j + 1 < nkv) swrite(buf ^ 1);
     __syncthreads();
   }
@@ -352,9 +394,7 @@ void fwd_bf16_kernel(FwdArgs a) {
           const float x0 = acc[qb][dt][4 * g + 0] * inv, x1 = acc[qb][dt][4 * g + 1] * inv;
           const float x2 = acc[qb][dt][4 * g + 2] * inv, x3 = acc[qb][dt][4 * g + 3] * inv;
           if (FULLD) {
-            u32x2 w;
-            w[0] = pack_bf16x2(x0, x1);
-            w[1] = pack_bf16x2(x2, x3);
+            const u32x2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
             *(u32x2*)(orow + col) = w;
           } else {
             const float xs[4] = {x0, x1, x2, x3};
@@ -365,7 +405,7 @@ void fwd_bf16_kernel(FwdArgs a) {
         }
       if (a.lse != nullptr && hh == 0) {
         const float msub = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-        a.lse[(size_t)bh * N + qi] = (msub + __log2f(l_tot)) * 0.69314718055994531f;
+        a.lse[(size_t)bh * N + qi] = (msub + log2f(l_tot)) * 0.69314718055994531f;
       }
     }
   }
@@ -382,11 +422,13 @@ hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
 
 }  // namespace
 
-int bf16_rows_per_block(int d_pad) {
-  return d_pad == 64 ? Cfg<64>::NW * Cfg<64>::QW * 32 : Cfg<128>::NW * Cfg<128>::QW * 32;
+int bf16_rows_per_block(int d) {
+  if (d == 128) return bf16_d128_rows_per_block();
+  return d <= 64 ? Cfg<64>::NW * Cfg<64>::QW * 32 : Cfg<128>::NW * Cfg<128>::QW * 32;
 }
 
 hipError_t launch_bf16(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream) {
+  if (a.d == 128) return launch_bf16_d128(a, causal, stream);
   const bool fulld = (a.d == d_pad);
   if (d_pad == 64) return causal ? launch_one<64, true>(a, fulld, stream) : launch_one<64, false>(a, fulld, stream);
   return causal ? launch_one<128, true>(a, fulld, stream) : launch_one<128, false>(a, fulld, stream);

@@ -1,0 +1,378 @@
+// Fused forward pass of exact softmax attention, bf16, head width exactly 128: the tuned
+// gfx950 kernel for long sequences.
+//
+// Same arithmetic as the generic bf16 kernel (online softmax over key tiles: running max,
+// denominator and unnormalised numerator rescaled together when the max rises; liminalml.com
+// "FlashAttention", online update equations), with a schedule built for CDNA4:
+//
+// * 8 waves per workgroup, 32 query rows each (256 rows per workgroup), two waves per SIMD.
+//   The waves form two groups (waves 0-3 and 4-7, one wave of each group per SIMD) that run
+//   one phase apart. Every key tile j is handled in two phases per wave:
+//     M_j: S_j^T = K_j Q^T (16 MFMAs) and O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs)
+//     V_j: online-softmax update of S_j into P_j (exponentials and the other VALU work)
+//   separated by workgroup barriers. While one group is in an M phase the other is in a V
+//   phase, so each SIMD keeps its matrix unit busy with one wave while the other wave's
+//   vector work runs alongside.
+// * K and V tiles (64 keys x 128 features) go from HBM straight into LDS with
+//   global_load_lds_dwordx4 (no staging registers, no LDS write instructions) into rings of
+//   4 slots; tile j+2 is requested at the start of M_j. Each wave's load instruction fills
+//   1 KiB of LDS (lane l -> byte 16*l), so rows are stored unpadded and the 16-byte chunks of
+//   each row are XOR-swizzled: K chunk c of row r sits at c ^ (r & 15) (the 16-byte operand
+//   reads of 16 consecutive rows hit distinct banks), V chunk c at c ^ 4*(r & 3) (the
+//   transpose reads of 4 consecutive rows and two 16-feature halves hit distinct banks).
+// * Operand layouts are those of the generic kernel: S^T and O^T accumulators hold one query
+//   per lane, probabilities go from the S^T accumulator into the B operand of the second
+//   product without data movement, and V^T operands come from ds_read_b64_tr_b16.
+// * A tile is masked only where it must be (the causal diagonal, the ragged last tile): the
+//   mask overwrites scores with -inf, the rest of the update is shared. Key rows past N are
+//   loaded from row N-1 (finite data, weight 0).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int D = 128;          // head width
+constexpr int BC = 64;          // keys per tile
+constexpr int NW = 8;           // waves per workgroup
+constexpr int NT = NW * 64;
+constexpr int BR = NW * 32;     // query rows per workgroup
+constexpr int ROWB = D * 2;     // bytes per key row in LDS
+constexpr int TILEB = BC * ROWB;  // 16 KiB per K or V tile
+constexpr int SLOTS = 4;
+constexpr int VREGION = SLOTS * TILEB;          // V ring starts after the K ring (64 KiB)
+constexpr int LDS_BYTES = 2 * SLOTS * TILEB;    // 128 KiB
+constexpr int LOADS_PER_TILE = 2 * (TILEB / 16) / NT;  // DMA instructions per thread per tile (K + V) = 4
+constexpr float kRescaleThreshold = 8.0f;       // log2 units
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+// One 16-byte-per-lane global -> LDS load: lane l's data lands at LDS byte lds_addr + 16*l.
+// Issued through inline assembly so that the compiler's wait insertion does not treat every
+// later LDS read as dependent on it; completion is tracked by hand (phase_barrier).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
+}
+
+// Wait until at most `n` vector-memory operations of this wave are outstanding and all of
+// its LDS reads have returned.
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  constexpr int imm = (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// Barrier between phases. `ahead` = how many tiles this wave has requested beyond the last
+// tile that some wave reads in the coming phase: the DMA loads of those tiles may stay in
+// flight, everything older must have landed in LDS. The compiler does not see the LDS
+// writes of the DMA loads, so the barrier is also a compiler memory barrier.
+__device__ __forceinline__ void phase_barrier(int ahead) {
+  if (ahead >= 2) wait_vm_lgkm0<2 * LOADS_PER_TILE>();
+  else if (ahead == 1) wait_vm_lgkm0<LOADS_PER_TILE>();
+  else wait_vm_lgkm0<0>();
+  asm volatile("s_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(NT, 2)
+void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
+  const bool CAUSAL = causal_flag != 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
+  const int lr = lane & 31, hh = lane >> 5;
+  const int grp = wave >> 2;   // 0: runs ahead, 1: one phase behind
+  const int N = a.N;
+
+  const int id = blockIdx.x;
+  const int qt_rev = id / a.BH;
+  const int bh = id - qt_rev * a.BH;
+  const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
+  const int q0 = qt * BR;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* __restrict__ Qh = (const uint16_t*)a.q + head;
+  const uint8_t* __restrict__ Kb = (const uint8_t*)((const uint16_t*)a.k + head);
+  const uint8_t* __restrict__ Vb = (const uint8_t*)((const uint16_t*)a.v + head);
+  uint16_t* __restrict__ Oh = (uint16_t*)a.o + head;
+
+  const int wq_lo = q0 + wave * 32;
+  const int wq_hi = wq_lo + 31;
+  const int qi = wq_lo + lr;
+
+  // ---- Q operand fragments (B operand of S^T = K Q^T) ---------------------------------------
+  u32x4 qf[D / 16];
+  {
+    const uint32_t negmask = a.neg ? 0x80008000u : 0u;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qi < N) x = *(const u32x4*)(Qh + (size_t)qi * D + 16 * kk + 8 * hh);
+      qf[kk] = x ^ negmask;
+    }
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+  const int nkv = (kv_end + BC - 1) / BC;
+  const int j_last = CAUSAL ? min(nkv - 1, wq_hi / BC) : nkv - 1;   // last tile this wave uses
+
+  // ---- LDS DMA addressing ----------------------------------------------------------------
+  // Each thread issues 2 K and 2 V load instructions per tile. For instruction i the wave
+  // fills LDS bytes [(2*wave+i)*1024, +1024) of the slot; lane l writes physical chunk l%16
+  // of row (2*wave+i)*4 + l/16 and so fetches the logical chunk the swizzle places there.
+  uint32_t gk_off[2], gv_off[2];
+  int dma_row[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = (2 * wave + i) * 4 + (lane >> 4);
+    const int phys = lane & 15;
+    dma_row[i] = row;
+    gk_off[i] = (uint32_t)(row * ROWB + ((phys ^ (row & 15)) * 16));
+    gv_off[i] = (uint32_t)(row * ROWB + ((phys ^ ((row & 3) << 2)) * 16));
+  }
+  // LDS byte address of the buffer (address-space cast, then the 32-bit LDS offset)
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
+  const uint32_t dma_lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_base + (uint32_t)(2 * wave * 1024)));
+  int last_issued = -1;
+  auto issue_tile = [&](int t) {
+    last_issued = t;
+    const int key0 = t * BC;
+    const uint32_t slot = (uint32_t)(t & (SLOTS - 1)) * TILEB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      uint32_t goff_k = gk_off[i] + (uint32_t)key0 * ROWB;
+      uint32_t goff_v = gv_off[i] + (uint32_t)key0 * ROWB;
+      if (key0 + dma_row[i] >= N) {   // rows past the end read row N-1 instead (weight 0 later)
+        const uint32_t back = (uint32_t)(key0 + dma_row[i] - (N - 1)) * ROWB;
+        goff_k -= back;
+        goff_v -= back;
+      }
+      const uint32_t ldst = dma_lds + slot + (uint32_t)(i * 1024);
+      dma16(Kb, goff_k, ldst);
+      dma16(Vb, goff_v, ldst + VREGION);
+    }
+  };
+
+  // ---- LDS read addressing -----------------------------------------------------------------
+  // K operand for step kk: row lr (+32 for the second 32-key block), logical chunk 2kk+hh.
+  uint32_t koff[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    koff[kk] = lds_base + (uint32_t)(lr * ROWB + (((2 * kk + hh) ^ (lr & 15)) * 16));
+  // V transpose reads: in each 16-lane group, lane 4r+q reads key row r (+8 for the second
+  // read) at features 4q..4q+3 of the 16-wide half b of 32-feature block dt.
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int b16 = (lane >> 4) & 1;
+  uint32_t voff[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int chunk = (4 * dt + 2 * b16 + ((lane & 3) >> 1)) ^ ((tr_row & 3) << 2);
+    voff[dt] = lds_base + VREGION + (uint32_t)(tr_row * ROWB + chunk * 16 + 8 * (lane & 1));
+  }
+
+  // ---- state -------------------------------------------------------------------------------
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 s0, s1;             // S_j^T for the two 32-key blocks of the current tile
+  u32x4 pb[BC / 16];          // P_{j}, bf16, B operand chunks (consumed in M_{j+1})
+
+  // Phase intervals are numbered k = 0, 1, 2, ...: group 0 runs M_j in interval 2j and V_j in
+  // 2j+1, group 1 one interval later. In interval k+1 the newest tile any wave reads is
+  // (k+1)/2 (K of an M phase; V of M_j is tile j-1), so the barrier closing interval k needs
+  // every tile up to (k+1)/2 in LDS.
+  auto barrier_after = [&](int k) { phase_barrier(last_issued - ((k + 1) >> 1)); };
+
+  // prologue: every wave requests its share of tiles 0 and 1; tile 0 lands before interval 0
+  issue_tile(0);
+  if (nkv > 1) issue_tile(1);
+  phase_barrier(last_issued);
+
+  // S_j^T = K_j Q^T. Reads run two steps ahead of the MFMAs; the scheduling barriers keep
+  // the compiler from sinking them next to their uses.
+  auto s_product = [&](int j) {
+    const uint32_t kslot = (uint32_t)(j & (SLOTS - 1)) * TILEB;
+    u32x4 kb0[D / 16], kb1[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      kb0[kk] = *(const lds_u32x4*)(uintptr_t)(koff[kk] + kslot);
+      kb1[kk] = *(const lds_u32x4*)(uintptr_t)(koff[kk] + kslot + 32 * ROWB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 c0 = {}, c1 = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      if (kk + 2 < D / 16) {
+        kb0[kk + 2] = *(const lds_u32x4*)(uintptr_t)(koff[kk + 2] + kslot);
+        kb1[kk + 2] = *(const lds_u32x4*)(uintptr_t)(koff[kk + 2] + kslot + 32 * ROWB);
+      }
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kb0[kk]),
+                                                   __builtin_bit_cast(bf16x8, qf[kk]), c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kb1[kk]),
+                                                   __builtin_bit_cast(bf16x8, qf[kk]), c1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s0 = c0;
+    s1 = c1;
+  };
+
+  // O^T += V_j^T P_j^T: 16 MFMAs over (16-key chunk, 32-feature block), reads two MFMAs ahead.
+  auto pv_product = [&](int j) {
+    const uint32_t vslot = (uint32_t)(j & (SLOTS - 1)) * TILEB;
+    constexpr int STEPS = (BC / 16) * (D / 32);
+    u32x4 av[STEPS];
+    auto load_step = [&](int st) {
+      const int c16 = st / (D / 32), dt = st % (D / 32);
+      const uint32_t addr = voff[dt] + vslot + (uint32_t)(c16 * 16 * ROWB);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 8 * ROWB));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      av[st] = (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
+    };
+    load_step(0);
+    load_step(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      if (st + 2 < STEPS) load_step(st + 2);
+      const int c16 = st / (D / 32), dt = st % (D / 32);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[st]),
+                                                        __builtin_bit_cast(bf16x8, pb[c16]), acc[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // M phase of tile j (j may equal nkv: then only the product with V_{j-1} remains).
+  auto m_phase = [&](int j) {
+    if (j + 2 < nkv) issue_tile(j + 2);
+    if (j < nkv && j <= j_last) s_product(j);
+    if (j >= 1 && j - 1 <= j_last) pv_product(j - 1);
+  };
+
+  // V phase of tile j: online-softmax update of S_j into P_j.
+  auto v_phase = [&](int j) {
+    if (j > j_last) return;
+    const int key0 = j * BC;
+    const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq_lo);
+    if (masked) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (key >= N || (CAUSAL && key > qi)) s0[i] = -INFINITY;
+        if (key + 32 >= N || (CAUSAL && key + 32 > qi)) s1[i] = -INFINITY;
+      }
+    }
+    float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) {
+      m0 = fmaxf(m0, fmaxf(s0[i], s0[i + 1]));
+      m1 = fmaxf(m1, fmaxf(s1[i], s1[i + 1]));
+    }
+    const float mt = pair_max(fmaxf(m0, m1) * a.sl2);
+    const float m_new = fmaxf(m_run, mt);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThreshold)) {
+      const float alpha = exp2f(m_run - m_new);   // 0 while m_run is -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm("v_mul_f32 %0, %0, %1" : "+v"(acc[dt][i]) : "v"(alpha));
+      m_run = m_new;
+    }
+    const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float p[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.sl2, -msub));
+      p[16 + i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.sl2, -msub));
+      ls[i & 3] += p[i] + p[16 + i];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = {pack_bf16x2(p[8 * c + 0], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
+                       pack_bf16x2(p[8 * c + 4], p[8 * c + 5]), pack_bf16x2(p[8 * c + 6], p[8 * c + 7])};
+      pb[c] = w;
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  // Phases: M_0 V_0 M_1 V_1 ... M_{n-1} V_{n-1} M_n, one barrier after each. Group 1 starts
+  // with one extra barrier and skips the barrier after its last phase, so it always works one
+  // phase behind group 0 while both pass the same number of barriers.
+  const int lag = grp;   // interval of this wave's M_0
+  if (grp == 1) barrier_after(0);
+  for (int j = 0; j < nkv; ++j) {
+    m_phase(j);
+    barrier_after(2 * j + lag);
+    v_phase(j);
+    barrier_after(2 * j + 1 + lag);
+  }
+  m_phase(nkv);
+  if (grp == 0) barrier_after(2 * nkv);
+  wait_vm_lgkm0<0>();
+
+  // ---- epilogue: o = u / l, lse = (m + log2 l) * ln 2 -----------------------------------------
+  const float l_tot = pair_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (qi < N) {
+    uint16_t* orow = Oh + (size_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = dt * 32 + 8 * g + 4 * hh;
+        const u32x2 w = {pack_bf16x2(acc[dt][4 * g + 0] * inv, acc[dt][4 * g + 1] * inv),
+                         pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
+        *(u32x2*)(orow + col) = w;
+      }
+    if (a.lse != nullptr && hh == 0) {
+      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+      a.lse[(size_t)bh * N + qi] = (msub + log2f(l_tot)) * 0.69314718055994531f;
+    }
+  }
+}
+
+}  // namespace
+
+int bf16_d128_rows_per_block() { return BR; }
+
+hipError_t launch_bf16_d128(const FwdArgs& a, bool causal, hipStream_t stream) {
+  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3((unsigned)(a.BH * a.n_qtiles)), dim3(NT), 0, stream, a,
+                     causal ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace fa

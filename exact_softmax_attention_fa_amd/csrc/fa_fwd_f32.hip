@@ -267,8 +267,8 @@ hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
 
 }  // namespace
 
-int f32_rows_per_block(int d_pad) {
-  return d_pad == 64 ? CfgF<64>::NW * 32 : CfgF<128>::NW * 32;
+int f32_rows_per_block(int d) {
+  return d <= 64 ? CfgF<64>::NW * 32 : CfgF<128>::NW * 32;
 }
 
 hipError_t launch_f32(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream) {

@@ -21,12 +21,18 @@ struct FwdArgs {
   int neg;        // 1 when scale < 0: the kernel negates q (exact) and uses |scale|
 };
 
-// Rows of queries per workgroup for each kernel family (host needs it for the grid).
-int bf16_rows_per_block(int d_pad);
-int f32_rows_per_block(int d_pad);
+// Rows of queries per workgroup of the kernel that will run for head width d (host needs it
+// for the grid).
+int bf16_rows_per_block(int d);
+int f32_rows_per_block(int d);
 
-// Enqueue one forward pass. d_pad is 64 or 128. Return hipSuccess or the launch error.
+// Enqueue one forward pass. d_pad (64 or 128) is the padded head width of the generic
+// kernels. Return hipSuccess or the launch error.
 hipError_t launch_bf16(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream);
 hipError_t launch_f32(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream);
+
+// Tuned bf16 kernel for head width exactly 128 (rows per workgroup, launch).
+int bf16_d128_rows_per_block();
+hipError_t launch_bf16_d128(const FwdArgs& a, bool causal, hipStream_t stream);
 
 }  // namespace fa
