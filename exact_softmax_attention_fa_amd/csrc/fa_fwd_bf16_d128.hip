@@ -73,6 +73,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
+template <int V> struct IntC { static constexpr int value = V; };
+
 // One 16-byte-per-lane global -> LDS load: lane l's data lands at LDS byte lds_addr + 16*l.
 // Issued through inline assembly so that the compiler's wait insertion does not treat every
 // later LDS read as dependent on it; completion is tracked by hand (phase_barrier).
@@ -149,6 +151,8 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // Each thread issues 2 K and 2 V load instructions per tile. For instruction i the wave
   // fills LDS bytes [(2*wave+i)*1024, +1024) of the slot; lane l writes physical chunk l%16
   // of row (2*wave+i)*4 + l/16 and so fetches the logical chunk the swizzle places there.
+  // The per-lane byte offsets inside a tile are fixed; the tile's base address advances in
+  // scalar registers, so issuing a whole tile costs no vector instructions.
   uint32_t gk_off[2], gv_off[2];
   int dma_row[2];
 #pragma unroll
@@ -163,26 +167,33 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
   const uint32_t dma_lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_base + (uint32_t)(2 * wave * 1024)));
   int last_issued = -1;
-  auto issue_tile = [&](int t) {
+  auto issue_tile = [&](int t) __attribute__((always_inline)) {
     last_issued = t;
     const int key0 = t * BC;
     const uint32_t slot = (uint32_t)(t & (SLOTS - 1)) * TILEB;
+    const uint8_t* kt = Kb + (size_t)key0 * ROWB;
+    const uint8_t* vt = Vb + (size_t)key0 * ROWB;
+    if (key0 + BC <= N) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      uint32_t goff_k = gk_off[i] + (uint32_t)key0 * ROWB;
-      uint32_t goff_v = gv_off[i] + (uint32_t)key0 * ROWB;
-      if (key0 + dma_row[i] >= N) {   // rows past the end read row N-1 instead (weight 0 later)
-        const uint32_t back = (uint32_t)(key0 + dma_row[i] - (N - 1)) * ROWB;
-        goff_k -= back;
-        goff_v -= back;
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t ldst = dma_lds + slot + (uint32_t)(i * 1024);
+        dma16(kt, gk_off[i], ldst);
+        dma16(vt, gv_off[i], ldst + VREGION);
       }
-      const uint32_t ldst = dma_lds + slot + (uint32_t)(i * 1024);
-      dma16(Kb, goff_k, ldst);
-      dma16(Vb, goff_v, ldst + VREGION);
+    } else {   // ragged last tile: rows past the end read row N-1 instead (weight 0 later)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int over = key0 + dma_row[i] - (N - 1);
+        const uint32_t back = over > 0 ? (uint32_t)over * ROWB : 0u;
+        const uint32_t ldst = dma_lds + slot + (uint32_t)(i * 1024);
+        dma16(kt, gk_off[i] - back, ldst);
+        dma16(vt, gv_off[i] - back, ldst + VREGION);
+      }
     }
   };
 
   // ---- LDS read addressing -----------------------------------------------------------------
+  // Per-lane byte addresses for slot 0; slot and block offsets are compile-time immediates.
   // K operand for step kk: row lr (+32 for the second 32-key block), logical chunk 2kk+hh.
   uint32_t koff[D / 16];
 #pragma unroll
@@ -213,31 +224,32 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // 2j+1, group 1 one interval later. In interval k+1 the newest tile any wave reads is
   // (k+1)/2 (K of an M phase; V of M_j is tile j-1), so the barrier closing interval k needs
   // every tile up to (k+1)/2 in LDS.
-  auto barrier_after = [&](int k) { phase_barrier(last_issued - ((k + 1) >> 1)); };
+  auto barrier_after = [&](int k) __attribute__((always_inline)) { phase_barrier(last_issued - ((k + 1) >> 1)); };
 
   // prologue: every wave requests its share of tiles 0 and 1; tile 0 lands before interval 0
   issue_tile(0);
   if (nkv > 1) issue_tile(1);
   phase_barrier(last_issued);
 
-  // S_j^T = K_j Q^T. Reads run two steps ahead of the MFMAs; the scheduling barriers keep
-  // the compiler from sinking them next to their uses.
-  auto s_product = [&](int j) {
-    const uint32_t kslot = (uint32_t)(j & (SLOTS - 1)) * TILEB;
-    u32x4 kb0[D / 16], kb1[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+  // S_j^T = K_j Q^T from LDS slot KS. Operand reads run PF steps ahead of the MFMAs;
+  // scheduling barriers keep the compiler from sinking them next to their uses.
+  constexpr int PF = 3;
+  auto s_product = [&](auto ks_tag) __attribute__((always_inline)) {
+    constexpr uint32_t kslot = decltype(ks_tag)::value * TILEB;
+    constexpr int STEPS = D / 16;
+    u32x4 kb0[STEPS], kb1[STEPS];
+    auto load_step = [&](int kk) __attribute__((always_inline)) {
       kb0[kk] = *(const lds_u32x4*)(uintptr_t)(koff[kk] + kslot);
-      kb1[kk] = *(const lds_u32x4*)(uintptr_t)(koff[kk] + kslot + 32 * ROWB);
-    }
+      kb1[kk] = *(const lds_u32x4*)(uintptr_t)(koff[kk] + (kslot + 32 * ROWB));
+    };
+#pragma unroll
+    for (int kk = 0; kk < PF; ++kk) load_step(kk);
     __builtin_amdgcn_sched_barrier(0);
     f32x16 c0 = {}, c1 = {};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      if (kk + 2 < D / 16) {
-        kb0[kk + 2] = *(const lds_u32x4*)(uintptr_t)(koff[kk + 2] + kslot);
-        kb1[kk + 2] = *(const lds_u32x4*)(uintptr_t)(koff[kk + 2] + kslot + 32 * ROWB);
-      }
+    for (int kk = 0; kk < STEPS; ++kk) {
+      if (kk + PF < STEPS) load_step(kk + PF);
+      __builtin_amdgcn_sched_barrier(0);
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kb0[kk]),
                                                    __builtin_bit_cast(bf16x8, qf[kk]), c0, 0, 0, 0);
       c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kb1[kk]),
@@ -248,25 +260,26 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
     s1 = c1;
   };
 
-  // O^T += V_j^T P_j^T: 16 MFMAs over (16-key chunk, 32-feature block), reads two MFMAs ahead.
-  auto pv_product = [&](int j) {
-    const uint32_t vslot = (uint32_t)(j & (SLOTS - 1)) * TILEB;
+  // O^T += V^T P^T from LDS slot VS: 16 MFMAs over (16-key chunk, 32-feature block).
+  auto pv_product = [&](auto vs_tag) __attribute__((always_inline)) {
+    constexpr uint32_t vslot = decltype(vs_tag)::value * TILEB;
     constexpr int STEPS = (BC / 16) * (D / 32);
     u32x4 av[STEPS];
-    auto load_step = [&](int st) {
+    auto load_step = [&](int st) __attribute__((always_inline)) {
       const int c16 = st / (D / 32), dt = st % (D / 32);
-      const uint32_t addr = voff[dt] + vslot + (uint32_t)(c16 * 16 * ROWB);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 8 * ROWB));
+      const uint32_t off = vslot + (uint32_t)(c16 * 16 * ROWB);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(voff[dt] + off));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(voff[dt] + (off + 8 * ROWB)));
       const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
       av[st] = (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
     };
-    load_step(0);
-    load_step(1);
+#pragma unroll
+    for (int st = 0; st < PF; ++st) load_step(st);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
-      if (st + 2 < STEPS) load_step(st + 2);
+      if (st + PF < STEPS) load_step(st + PF);
+      __builtin_amdgcn_sched_barrier(0);
       const int c16 = st / (D / 32), dt = st % (D / 32);
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[st]),
                                                         __builtin_bit_cast(bf16x8, pb[c16]), acc[dt], 0, 0, 0);
@@ -274,15 +287,20 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
     }
   };
 
-  // M phase of tile j (j may equal nkv: then only the product with V_{j-1} remains).
-  auto m_phase = [&](int j) {
+  // M phase of tile j held in LDS slot SLOT (j may equal nkv: then only the product with
+  // V_{j-1} remains). The wave raises its issue priority so that the other wave's vector
+  // work on the same SIMD does not hold back its MFMA stream.
+  auto m_phase = [&](int j, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_tag)::value;
+    __builtin_amdgcn_s_setprio(2);
     if (j + 2 < nkv) issue_tile(j + 2);
-    if (j < nkv && j <= j_last) s_product(j);
-    if (j >= 1 && j - 1 <= j_last) pv_product(j - 1);
+    if (j < nkv && j <= j_last) s_product(IntC<SL>{});
+    if (j >= 1 && j - 1 <= j_last) pv_product(IntC<(SL + SLOTS - 1) % SLOTS>{});
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // V phase of tile j: online-softmax update of S_j into P_j.
-  auto v_phase = [&](int j) {
+  auto v_phase = [&](int j) __attribute__((always_inline)) {
     if (j > j_last) return;
     const int key0 = j * BC;
     const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq_lo);
@@ -312,14 +330,15 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
       m_run = m_new;
     }
     const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float p[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       p[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.sl2, -msub));
       p[16 + i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.sl2, -msub));
-      ls[i & 3] += p[i] + p[16 + i];
     }
+    float ls[4] = {p[0] + p[16], p[1] + p[17], p[2] + p[18], p[3] + p[19]};
+#pragma unroll
+    for (int i = 4; i < 16; ++i) ls[i & 3] += p[i] + p[16 + i];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const u32x4 w = {pack_bf16x2(p[8 * c + 0], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
@@ -331,16 +350,32 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
 
   // Phases: M_0 V_0 M_1 V_1 ... M_{n-1} V_{n-1} M_n, one barrier after each. Group 1 starts
   // with one extra barrier and skips the barrier after its last phase, so it always works one
-  // phase behind group 0 while both pass the same number of barriers.
+  // phase behind group 0 while both pass the same number of barriers. The loop is unrolled by
+  // the ring size so that every LDS slot offset is an immediate.
   const int lag = grp;   // interval of this wave's M_0
   if (grp == 1) barrier_after(0);
-  for (int j = 0; j < nkv; ++j) {
-    m_phase(j);
+  auto tile = [&](int j, auto slot_tag) __attribute__((always_inline)) {
+    m_phase(j, slot_tag);
     barrier_after(2 * j + lag);
     v_phase(j);
     barrier_after(2 * j + 1 + lag);
+  };
+  int j = 0;
+  for (; j + SLOTS <= nkv; j += SLOTS) {
+    tile(j, IntC<0>{});
+    tile(j + 1, IntC<1>{});
+    tile(j + 2, IntC<2>{});
+    tile(j + 3, IntC<3>{});
   }
-  m_phase(nkv);
+  if (j < nkv) tile(j++, IntC<0>{});
+  if (j < nkv) tile(j++, IntC<1>{});
+  if (j < nkv) tile(j++, IntC<2>{});
+  switch (nkv & (SLOTS - 1)) {   // the final M phase (product with V_{nkv-1} only)
+    case 0: m_phase(nkv, IntC<0>{}); break;
+    case 1: m_phase(nkv, IntC<1>{}); break;
+    case 2: m_phase(nkv, IntC<2>{}); break;
+    default: m_phase(nkv, IntC<3>{}); break;
+  }
   if (grp == 0) barrier_after(2 * nkv);
   wait_vm_lgkm0<0>();
 
