@@ -39,7 +39,9 @@ KERNEL_SOURCES = ["exact_softmax_attention_fa_amd/csrc/fa_fwd_bf16.hip",
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
 # dispatch), each scaled by the factor the same counter reads for a plain copy of known size.
 # Keyed by workload; valid only for the kernel sources whose hash is stored with them.
-TRAFFIC = {}
+TRAFFIC = {
+    "fwd_bf16_b1_h16_n8192_d128_widek": {"bytes": 202210303, "kernel_hash": "6468d91aef76b2f9"},
+}
 
 
 def kernel_hash() -> str:
