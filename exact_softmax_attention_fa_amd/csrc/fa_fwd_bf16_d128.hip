@@ -15,7 +15,8 @@
 //   vector work runs alongside.
 // * K and V tiles (64 keys x 128 features) go from HBM straight into LDS with
 //   global_load_lds_dwordx4 (no staging registers, no LDS write instructions) into rings of
-//   4 slots; tile j+2 is requested at the start of M_j. Each wave's load instruction fills
+//   4 slots, requested at the end of V phases (two tiles ahead for the leading group, three for
+//   the other), where the vector work leaves issue slack. Each wave's load instruction fills
 //   1 KiB of LDS (lane l -> byte 16*l), so rows are stored unpadded and the 16-byte chunks of
 //   each row are XOR-swizzled: K chunk c of row r sits at c ^ (r & 15) (the 16-byte operand
 //   reads of 16 consecutive rows hit distinct banks), V chunk c at c ^ 4*(r & 3) (the
@@ -23,6 +24,13 @@
 // * Operand layouts are those of the generic kernel: S^T and O^T accumulators hold one query
 //   per lane, probabilities go from the S^T accumulator into the B operand of the second
 //   product without data movement, and V^T operands come from ds_read_b64_tr_b16.
+// * The softmax of a tile takes no row maximum in the common case: the exponentials use the
+//   running reference directly, and only when the tile's sum shows a score far above it (more
+//   than 2^59 in probability terms, or the first tile) is the tile maximum taken and the
+//   reference raised, with the usual rescale of denominator and numerator. Probabilities then
+//   stay below 2^64, far inside the fp32 and bf16 ranges; the reference is any value at or
+//   below the true running maximum, which leaves u / l and the log-normaliser unchanged up to
+//   rounding.
 // * A tile is masked only where it must be (the causal diagonal, the ragged last tile): the
 //   mask overwrites scores with -inf, the rest of the update is shared. Key rows past N are
 //   loaded from row N-1 (finite data, weight 0).
@@ -58,7 +66,11 @@ constexpr int SLOTS = 4;
 constexpr int VREGION = SLOTS * TILEB;          // V ring starts after the K ring (64 KiB)
 constexpr int LDS_BYTES = 2 * SLOTS * TILEB;    // 128 KiB
 constexpr int LOADS_PER_TILE = 2 * (TILEB / 16) / NT;  // DMA instructions per thread per tile (K + V) = 4
-constexpr float kRescaleThreshold = 8.0f;       // log2 units
+// A tile whose per-lane probability sum exceeds 2^64 raises the reference (see v_phase).
+constexpr float kRaiseSum = 18446744073709551616.0f;   // 2^64
+// Reference before the first tile: finite (so that masked scores give exp2(-inf) = 0, never
+// a NaN), and so low that the first tile always raises it.
+constexpr float kRefInit = -1.0e30f;
 
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -216,7 +228,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = kRefInit, l_run = 0.0f;
   f32x16 s0, s1;             // S_j^T for the two 32-key blocks of the current tile
   u32x4 pb[BC / 16];          // P_{j}, bf16, B operand chunks (consumed in M_{j+1})
 
@@ -224,16 +236,24 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // 2j+1, group 1 one interval later. In interval k+1 the newest tile any wave reads is
   // (k+1)/2 (K of an M phase; V of M_j is tile j-1), so the barrier closing interval k needs
   // every tile up to (k+1)/2 in LDS.
+  // Loads are issued at the end of V phases, where the vector work leaves issue slack: group 0
+  // requests tile j+2 after V_j (interval 2j+1), group 1 tile j+3 after its V_j (interval
+  // 2j+2). Tile t goes to the slot of tile t-4, whose last readers (the V products of M_{t-3})
+  // ran in intervals 2t-6 and 2t-5, before either request.
   auto barrier_after = [&](int k) __attribute__((always_inline)) { phase_barrier(last_issued - ((k + 1) >> 1)); };
 
   // prologue: every wave requests its share of tiles 0 and 1; tile 0 lands before interval 0
   issue_tile(0);
   if (nkv > 1) issue_tile(1);
+  if (grp == 1 && nkv > 2) issue_tile(2);
   phase_barrier(last_issued);
 
   // S_j^T = K_j Q^T from LDS slot KS. Operand reads run PF steps ahead of the MFMAs;
   // scheduling barriers keep the compiler from sinking them next to their uses.
-  constexpr int PF = 3;
+#ifndef FA_PF
+#define FA_PF 3
+#endif
+  constexpr int PF = FA_PF;
   auto s_product = [&](auto ks_tag) __attribute__((always_inline)) {
     constexpr uint32_t kslot = decltype(ks_tag)::value * TILEB;
     constexpr int STEPS = D / 16;
@@ -293,13 +313,17 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   auto m_phase = [&](int j, auto slot_tag) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_tag)::value;
     __builtin_amdgcn_s_setprio(2);
-    if (j + 2 < nkv) issue_tile(j + 2);
     if (j < nkv && j <= j_last) s_product(IntC<SL>{});
     if (j >= 1 && j - 1 <= j_last) pv_product(IntC<(SL + SLOTS - 1) % SLOTS>{});
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // V phase of tile j: online-softmax update of S_j into P_j.
+  // V phase of tile j: online-softmax update of S_j into P_j. The exponentials use the current
+  // reference m_run directly; no per-tile maximum is taken unless the tile's sum shows that
+  // the reference must be raised (some score more than ~2^59 above it, or the first tile,
+  // whose reference is a huge negative number): then the tile maximum is found, the
+  // denominator and numerator are rescaled and the exponentials are recomputed. Otherwise
+  // every probability is at most 2^64, so the fp32 sums and bf16 probabilities stay finite.
   auto v_phase = [&](int j) __attribute__((always_inline)) {
     if (j > j_last) return;
     const int key0 = j * BC;
@@ -312,40 +336,43 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
         if (key + 32 >= N || (CAUSAL && key + 32 > qi)) s1[i] = -INFINITY;
       }
     }
-    float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
+    float p[32], ls;
+    auto exps = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) {
-      m0 = fmaxf(m0, fmaxf(s0[i], s0[i + 1]));
-      m1 = fmaxf(m1, fmaxf(s1[i], s1[i + 1]));
-    }
-    const float mt = pair_max(fmaxf(m0, m1) * a.sl2);
-    const float m_new = fmaxf(m_run, mt);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThreshold)) {
-      const float alpha = exp2f(m_run - m_new);   // 0 while m_run is -inf
+      for (int i = 0; i < 16; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.sl2, -m_run));
+        p[16 + i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.sl2, -m_run));
+      }
+      float t[4] = {p[0] + p[16], p[1] + p[17], p[2] + p[18], p[3] + p[19]};
+#pragma unroll
+      for (int i = 4; i < 16; ++i) t[i & 3] += p[i] + p[16 + i];
+      ls = (t[0] + t[1]) + (t[2] + t[3]);
+    };
+    exps();
+    if (__builtin_amdgcn_ballot_w64(ls > kRaiseSum)) {
+      float m0 = fmaxf(s0[0], s0[1]), m1 = fmaxf(s1[0], s1[1]);
+#pragma unroll
+      for (int i = 2; i < 16; i += 2) {
+        m0 = fmaxf(m0, fmaxf(s0[i], s0[i + 1]));
+        m1 = fmaxf(m1, fmaxf(s1[i], s1[i + 1]));
+      }
+      const float m_new = fmaxf(m_run, pair_max(fmaxf(m0, m1) * a.sl2));
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) asm("v_mul_f32 %0, %0, %1" : "+v"(acc[dt][i]) : "v"(alpha));
       m_run = m_new;
+      exps();
     }
-    const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-    float p[32];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.sl2, -msub));
-      p[16 + i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.sl2, -msub));
-    }
-    float ls[4] = {p[0] + p[16], p[1] + p[17], p[2] + p[18], p[3] + p[19]};
-#pragma unroll
-    for (int i = 4; i < 16; ++i) ls[i & 3] += p[i] + p[16 + i];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const u32x4 w = {pack_bf16x2(p[8 * c + 0], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
                        pack_bf16x2(p[8 * c + 4], p[8 * c + 5]), pack_bf16x2(p[8 * c + 6], p[8 * c + 7])};
       pb[c] = w;
     }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    l_run += ls;
   };
 
   // Phases: M_0 V_0 M_1 V_1 ... M_{n-1} V_{n-1} M_n, one barrier after each. Group 1 starts
@@ -358,6 +385,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
     m_phase(j, slot_tag);
     barrier_after(2 * j + lag);
     v_phase(j);
+    if (j + 2 + grp < nkv) issue_tile(j + 2 + grp);
     barrier_after(2 * j + 1 + lag);
   };
   int j = 0;
@@ -394,8 +422,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
         *(u32x2*)(orow + col) = w;
       }
     if (a.lse != nullptr && hh == 0) {
-      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-      a.lse[(size_t)bh * N + qi] = (msub + log2f(l_tot)) * 0.69314718055994531f;
+      a.lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
     }
   }
 }
