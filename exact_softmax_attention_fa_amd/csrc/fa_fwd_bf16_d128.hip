@@ -15,8 +15,8 @@
 //   vector work runs alongside.
 // * K and V tiles (64 keys x 128 features) go from HBM straight into LDS with
 //   global_load_lds_dwordx4 (no staging registers, no LDS write instructions) into rings of
-//   4 slots, requested at the end of V phases (two tiles ahead for the leading group, three for
-//   the other), where the vector work leaves issue slack. Each wave's load instruction fills
+//   4 slots, requested at the start of V phases (two tiles ahead for the leading group, three
+//   for the other), where the vector work leaves issue slack. Each wave's load instruction fills
 //   1 KiB of LDS (lane l -> byte 16*l), so rows are stored unpadded and the 16-byte chunks of
 //   each row are XOR-swizzled: K chunk c of row r sits at c ^ (r & 15) (the 16-byte operand
 //   reads of 16 consecutive rows hit distinct banks), V chunk c at c ^ 4*(r & 3) (the
@@ -236,10 +236,10 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // 2j+1, group 1 one interval later. In interval k+1 the newest tile any wave reads is
   // (k+1)/2 (K of an M phase; V of M_j is tile j-1), so the barrier closing interval k needs
   // every tile up to (k+1)/2 in LDS.
-  // Loads are issued at the end of V phases, where the vector work leaves issue slack: group 0
-  // requests tile j+2 after V_j (interval 2j+1), group 1 tile j+3 after its V_j (interval
-  // 2j+2). Tile t goes to the slot of tile t-4, whose last readers (the V products of M_{t-3})
-  // ran in intervals 2t-6 and 2t-5, before either request.
+  // Loads are issued at the start of V phases, where the vector work leaves issue slack: group
+  // 0 requests tile j+2 in V_j (interval 2j+1), group 1 tile j+3 in its V_j (interval 2j+2).
+  // Tile t goes to the slot of tile t-4, whose last readers (the V products of M_{t-3}) ran in
+  // intervals 2t-6 and 2t-5, before either request.
   auto barrier_after = [&](int k) __attribute__((always_inline)) { phase_barrier(last_issued - ((k + 1) >> 1)); };
 
   // prologue: every wave requests its share of tiles 0 and 1; tile 0 lands before interval 0
@@ -384,8 +384,8 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   auto tile = [&](int j, auto slot_tag) __attribute__((always_inline)) {
     m_phase(j, slot_tag);
     barrier_after(2 * j + lag);
-    v_phase(j);
     if (j + 2 + grp < nkv) issue_tile(j + 2 + grp);
+    v_phase(j);
     barrier_after(2 * j + 1 + lag);
   };
   int j = 0;
