@@ -57,13 +57,18 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max rises by > 2^8
 
+// Workgroups the key split aims for (a split doubles them while they stay at or below this).
+#ifndef FA_SPLIT_TARGET_WGS
+#define FA_SPLIT_TARGET_WGS 512
+#endif
+
 // Tile configuration per padded head width: QW query blocks of 32 per wave, NW waves per
 // workgroup, BC keys per LDS tile. The defaults can be overridden at build time for sweeps.
 #ifndef FA_BF16_D64_QW
-#define FA_BF16_D64_QW 2
+#define FA_BF16_D64_QW 1
 #endif
 #ifndef FA_BF16_D64_NW
-#define FA_BF16_D64_NW 4
+#define FA_BF16_D64_NW 2
 #endif
 #ifndef FA_BF16_D64_BC
 #define FA_BF16_D64_BC 64
@@ -79,17 +84,21 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max r
 #endif
 // minimum waves per SIMD the register allocation must allow (1: up to 512 registers)
 #ifndef FA_BF16_D64_WPE
-#define FA_BF16_D64_WPE 1
+#define FA_BF16_D64_WPE 2
 #endif
 #ifndef FA_BF16_D128_WPE
 #define FA_BF16_D128_WPE 2
 #endif
+// NW counts the waves of one key group; a workgroup runs SPLIT key groups (MAXSPLIT at most)
+// over the same queries and merges them at the end.
 template <int D> struct Cfg;
 template <> struct Cfg<64> {
   static constexpr int QW = FA_BF16_D64_QW, NW = FA_BF16_D64_NW, BC = FA_BF16_D64_BC, WPE = FA_BF16_D64_WPE;
+  static constexpr int MAXSPLIT = 4;
 };
 template <> struct Cfg<128> {
   static constexpr int QW = FA_BF16_D128_QW, NW = FA_BF16_D128_NW, BC = FA_BF16_D128_BC, WPE = FA_BF16_D128_WPE;
+  static constexpr int MAXSPLIT = 1;
 };
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -108,11 +117,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
-// 8 consecutive bf16 of one row, zero outside [0, d) (generic head width).
+// 8 consecutive bf16 of one row, zero outside [0, d) (generic head width). The loads are
+// unconditional (column clamped) so that they issue together.
 __device__ __forceinline__ u32x4 load8_masked(const uint16_t* row, int col, int d) {
   uint16_t e[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) e[t] = (col + t < d) ? row[col + t] : (uint16_t)0;
+  for (int t = 0; t < 8; ++t) {
+    const uint16_t x = row[min(col + t, d - 1)];
+    e[t] = (col + t < d) ? x : (uint16_t)0;
+  }
   u32x4 r;
   r[0] = e[0] | ((uint32_t)e[1] << 16);
   r[1] = e[2] | ((uint32_t)e[3] << 16);
@@ -233,24 +246,31 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
   }
 }
 
-template <int D, bool CAUSAL, bool FULLD>
-__global__ __launch_bounds__(Cfg<D>::NW * 64, Cfg<D>::WPE)
+template <int D, bool CAUSAL, bool FULLD, int SPLIT>
+__global__ __launch_bounds__(Cfg<D>::NW * SPLIT * 64, Cfg<D>::WPE)
 void fwd_bf16_kernel(FwdArgs a) {
   constexpr int QW = Cfg<D>::QW, NW = Cfg<D>::NW, BC = Cfg<D>::BC;
-  constexpr int NT = NW * 64;
+  constexpr int NT = NW * SPLIT * 64;
   constexpr int BR = NW * QW * 32;
   constexpr int KP = D + 8;    // K row pitch (elements): conflict-free 16-byte reads of 32 rows
   constexpr int VP = D + 16;   // V row pitch: conflict-free transpose reads of 4 rows
   constexpr int KT = BC * KP, VT = BC * VP;
   constexpr int CH = BC * D / 8;      // 16-byte chunks per K (or V) tile
-  constexpr int CPT = CH / NT;        // chunks per thread
-  static_assert(CH % NT == 0, "tile must split evenly over the workgroup");
+  constexpr int CPT = SPLIT * CH / NT;  // chunks per thread (SPLIT tiles per step)
+  static_assert((SPLIT * CH) % NT == 0, "tiles must split evenly over the workgroup");
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shapes");
+  // one value block per (query wave, extra key group) for the final merge
+  constexpr int NV = QW * (D / 32 * 16 + 2);
+  static_assert(SPLIT == 1 || NW * (SPLIT - 1) * NV * 64 * 4 <= 2 * SPLIT * (KT + VT) * 2,
+                "merge area must fit in the tile buffers");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SPLIT * (KT + VT)];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave_all = tid >> 6;
+  const int grpk = wave_all / NW;    // key group: takes tiles grpk, grpk + SPLIT, ...
+  const int wave = wave_all - grpk * NW;   // query wave within the workgroup
   const int lr = lane & 31, hh = lane >> 5;
   const int N = a.N, d = a.d;
 
@@ -272,21 +292,20 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int wq_hi = wq_lo + QW * 32 - 1;   // last query of this wave
 
   // Q fragments: B operand of S^T = K Q^T. Lane l supplies query l%32, features 16kk+8hh..+7.
+  // (unconditional loads from a clamped row, so that they are all in flight together;
+  // rows past N become 0)
   u32x4 qf[QW][D / 16];
   const uint32_t negmask = a.neg ? 0x80008000u : 0u;
 #pragma unroll
   for (int qb = 0; qb < QW; ++qb) {
     const int qi = wq_lo + qb * 32 + lr;
+    const uint16_t* qrow = Qh + (size_t)min(qi, N - 1) * d;
+    const uint32_t keep = qi < N ? 0xffffffffu : 0u;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const int col = 16 * kk + 8 * hh;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qi < N) {
-        if (FULLD) x = *(const u32x4*)(Qh + (size_t)qi * d + col);
-        else       x = load8_masked(Qh + (size_t)qi * d, col, d);
-      }
-      x ^= negmask;
-      qf[qb][kk] = x;
+      const u32x4 x = FULLD ? *(const u32x4*)(qrow + col) : load8_masked(qrow, col, d);
+      qf[qb][kk] = (x & keep) ^ negmask;
     }
   }
 
@@ -307,15 +326,16 @@ void fwd_bf16_kernel(FwdArgs a) {
   // Global -> register staging of one K/V tile. Chunk c covers row c/(D/8), features
   // 8*(c%(D/8))..+7; consecutive threads read consecutive 16-byte pieces of a row.
   u32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int j) {
-    const int key0 = j * BC;
-    const bool whole = FULLD && key0 + BC <= N;   // no bounds checks needed for this tile
+  // step `it` stages tiles it*SPLIT .. it*SPLIT + SPLIT-1 (one per key group)
+  auto gload = [&](int it) {
+    const int key_lo = it * SPLIT * BC;
+    const bool whole = FULLD && key_lo + SPLIT * BC <= N;   // no bounds checks needed
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + r * NT;
-      const int row = c / (D / 8);
+      const int row = c / (D / 8);      // row within the SPLIT*BC staged keys
       const int col = (c % (D / 8)) * 8;
-      const int key = key0 + row;
+      const int key = key_lo + row;
       if (whole) {
         kreg[r] = *(const u32x4*)(Kh + (size_t)key * d + col);
         vreg[r] = *(const u32x4*)(Vh + (size_t)key * d + col);
@@ -331,18 +351,21 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
   };
   auto swrite = [&](int buf) {
-    uint16_t* Ks = smem + buf * (KT + VT);
-    uint16_t* Vs = Ks + KT;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + r * NT;
       const int row = c / (D / 8);
       const int col = (c % (D / 8)) * 8;
-      *(u32x4*)(Ks + row * KP + col) = kreg[r];
-      *(u32x4*)(Vs + row * VP + col) = vreg[r];
+      uint16_t* Ks = smem + (buf * SPLIT + row / BC) * (KT + VT);
+      uint16_t* Vs = Ks + KT;
+      const int tr = row % BC;
+      *(u32x4*)(Ks + tr * KP + col) = kreg[r];
+      *(u32x4*)(Vs + tr * VP + col) = vreg[r];
     }
   };
+  auto tile_buf = [&](int buf) { return (const uint16_t*)smem + (buf * SPLIT + grpk) * (KT + VT); };
 
+  const int nit = (nkv + SPLIT - 1) / SPLIT;   // steps of SPLIT tiles
   gload(0);
   swrite(0);
   __syncthreads();
@@ -355,27 +378,76 @@ void fwd_bf16_kernel(FwdArgs a) {
   // Tiles [0, j_split) hold only keys that every query of the workgroup may see, so they
   // take the unmasked path with no per-tile decision; the remaining tiles (the causal
   // diagonal, or the ragged last tile) take the masked path, and under a causal mask a wave
-  // skips the tiles that lie entirely past its own last query.
+  // skips the tiles that lie entirely past its own last query. Key group g handles tiles
+  // it*SPLIT + g.
   const int j_split = CAUSAL ? min(N / BC, (q0 + 1) / BC) : N / BC;
-  int j = 0;
-  for (; j < j_split; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkv) gload(j + 1);
-    const uint16_t* Ks = smem + buf * (KT + VT);
-    tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, j * BC, N, wq_lo, a.sl2,
-                                               lr, hh, tr_row, tr_col);
-    if (j + 1 < nkv) swrite(buf ^ 1);
+  const int it_split = j_split / SPLIT;   // steps whose tiles are all unmasked
+  int it = 0;
+  for (; it < it_split; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nit) gload(it + 1);
+    const uint16_t* Ks = tile_buf(buf);
+    tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, (it * SPLIT + grpk) * BC, N,
+                                               wq_lo, a.sl2, lr, hh, tr_row, tr_col);
+    if (it + 1 < nit) swrite(buf ^ 1);
     __syncthreads();
   }
-  for (; j < nkv; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkv) gload(j + 1);
-    const uint16_t* Ks = smem + buf * (KT + VT);
-    if (!CAUSAL || j * BC <= wq_hi)
-      tile_step<D, QW, BC, KP, VP, true, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, j * BC, N, wq_lo, a.sl2,
+  for (; it < nit; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nit) gload(it + 1);
+    const uint16_t* Ks = tile_buf(buf);
+    const int t = it * SPLIT + grpk;
+    if (t < j_split)
+      tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, t * BC, N, wq_lo, a.sl2,
+                                                 lr, hh, tr_row, tr_col);
+    else if (t < nkv && (!CAUSAL || t * BC <= wq_hi))
+      tile_step<D, QW, BC, KP, VP, true, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, t * BC, N, wq_lo, a.sl2,
                                                 lr, hh, tr_row, tr_col);
-    if (j + 1 < nkv) swrite(buf ^ 1);
+    if (it + 1 < nit) swrite(buf ^ 1);
     __syncthreads();
+  }
+
+  // ---- merge of the key groups (split of the key range inside the workgroup) -------------
+  // Each group holds (m, l, u) for its keys; with m* = max m_g the row's state is
+  // l = sum l_g 2^(m_g - m*), u = sum u_g 2^(m_g - m*) (interactiveml.org, merge of the three
+  // sufficient statistics). Groups 1.. hand their state to group 0 through LDS (the tile
+  // buffers are free after the last barrier of the loop).
+  if constexpr (SPLIT > 1) {
+    float* mb = (float*)smem;
+    if (grpk > 0) {
+      float* dst = mb + (size_t)((wave * (SPLIT - 1) + grpk - 1) * NV) * 64 + lane;
+#pragma unroll
+      for (int qb = 0; qb < QW; ++qb) {
+        const int v0 = qb * (D / 32 * 16 + 2);
+        dst[(v0 + 0) * 64] = m_run[qb];
+        dst[(v0 + 1) * 64] = l_run[qb];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) dst[(v0 + 2 + dt * 16 + i) * 64] = acc[qb][dt][i];
+      }
+    }
+    __syncthreads();
+    if (grpk > 0) return;
+#pragma unroll
+    for (int g = 1; g < SPLIT; ++g) {
+      const float* src = mb + (size_t)((wave * (SPLIT - 1) + g - 1) * NV) * 64 + lane;
+#pragma unroll
+      for (int qb = 0; qb < QW; ++qb) {
+        const int v0 = qb * (D / 32 * 16 + 2);
+        const float mg = src[(v0 + 0) * 64], lg = src[(v0 + 1) * 64];
+        const float ms = fmaxf(m_run[qb], mg);
+        // weights 2^(m - m*); a group that saw no key has m = -inf and weight 0
+        const float w0 = (m_run[qb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[qb] - ms);
+        const float wg = (mg == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mg - ms);
+        l_run[qb] = l_run[qb] * w0 + lg * wg;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[qb][dt][i] = acc[qb][dt][i] * w0 + src[(v0 + 2 + dt * 16 + i) * 64] * wg;
+        m_run[qb] = ms;
+      }
+    }
   }
 
   // ---- epilogue: o = u / l, lse = (m + log2 l) * ln 2 ----------------------------------------
@@ -411,13 +483,34 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
+template <int D, bool CAUSAL, int SPLIT>
+hipError_t launch_split(const FwdArgs& a, bool fulld, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.BH * a.n_qtiles));
+  const dim3 block(Cfg<D>::NW * SPLIT * 64);
+  if (fulld) hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, SPLIT>), grid, block, 0, stream, a);
+  else       hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, SPLIT>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// Key groups per workgroup: split the key range when the grid alone leaves most compute
+// units idle and every group still gets at least two tiles.
+template <int D>
+int choose_split(const FwdArgs& a) {
+  const long long wgs = (long long)a.BH * a.n_qtiles;
+  const int nkv = (a.N + Cfg<D>::BC - 1) / Cfg<D>::BC;
+  int split = 1;
+  while (split * 2 <= Cfg<D>::MAXSPLIT && wgs * split * 2 <= FA_SPLIT_TARGET_WGS && nkv >= 2 * split * 2) split *= 2;
+  return split;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.BH * a.n_qtiles));
-  const dim3 block(Cfg<D>::NW * 64);
-  if (fulld) hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), grid, block, 0, stream, a);
-  else       hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  if constexpr (Cfg<D>::MAXSPLIT >= 4) {
+    const int split = choose_split<D>(a);
+    if (split == 4) return launch_split<D, CAUSAL, 4>(a, fulld, stream);
+    if (split == 2) return launch_split<D, CAUSAL, 2>(a, fulld, stream);
+  }
+  return launch_split<D, CAUSAL, 1>(a, fulld, stream);
 }
 
 }  // namespace

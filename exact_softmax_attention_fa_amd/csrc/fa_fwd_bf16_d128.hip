@@ -144,14 +144,16 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   const int qi = wq_lo + lr;
 
   // ---- Q operand fragments (B operand of S^T = K Q^T) ---------------------------------------
+  // (unconditional loads from a clamped row, all in flight together; rows past N become 0)
   u32x4 qf[D / 16];
   {
     const uint32_t negmask = a.neg ? 0x80008000u : 0u;
+    const uint32_t keep = qi < N ? 0xffffffffu : 0u;
+    const uint16_t* qrow = Qh + (size_t)min(qi, N - 1) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qi < N) x = *(const u32x4*)(Qh + (size_t)qi * D + 16 * kk + 8 * hh);
-      qf[kk] = x ^ negmask;
+      const u32x4 x = *(const u32x4*)(qrow + 16 * kk + 8 * hh);
+      qf[kk] = (x & keep) ^ negmask;
     }
   }
 

@@ -30,9 +30,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kRescaleThreshold = 8.0f;
 
+// NW waves per key group, BC keys per tile; a workgroup runs up to MAXSPLIT key groups over
+// the same queries (taking tiles g, g + SPLIT, ...) and merges them at the end.
 template <int D> struct CfgF;
-template <> struct CfgF<64>  { static constexpr int NW = 2, BC = 32; };
-template <> struct CfgF<128> { static constexpr int NW = 2, BC = 32; };
+template <> struct CfgF<64>  { static constexpr int NW = 1, BC = 32, MAXSPLIT = 4; };
+template <> struct CfgF<128> { static constexpr int NW = 1, BC = 32, MAXSPLIT = 2; };
 
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -43,31 +45,42 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 4 consecutive floats of one row, zero outside [0, d); the loads are unconditional (column
+// clamped) so that they issue together.
 __device__ __forceinline__ f32x4 load4_masked(const float* row, int col, int d) {
   f32x4 r;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) r[t] = (col + t < d) ? row[col + t] : 0.0f;
+  for (int t = 0; t < 4; ++t) {
+    const float x = row[min(col + t, d - 1)];
+    r[t] = (col + t < d) ? x : 0.0f;
+  }
   return r;
 }
 
-template <int D, bool CAUSAL, bool FULLD>
-__global__ __launch_bounds__(CfgF<D>::NW * 64, 1)
+template <int D, bool CAUSAL, bool FULLD, int SPLIT>
+__global__ __launch_bounds__(CfgF<D>::NW * SPLIT * 64, 1)
 void fwd_f32_kernel(FwdArgs a) {
   constexpr int NW = CfgF<D>::NW, BC = CfgF<D>::BC;
-  constexpr int NT = NW * 64;
+  constexpr int NT = NW * SPLIT * 64;
   constexpr int BR = NW * 32;
   constexpr int KP = D + 1;   // odd pitch: the 32 rows of one read fall in distinct banks
   constexpr int VP = D + 4;
   constexpr int KT = BC * KP, VT = BC * VP;
   constexpr int CH = BC * D / 4;   // 16-byte chunks per tile
-  constexpr int CPT = CH / NT;
+  constexpr int CPT = SPLIT * CH / NT;   // SPLIT tiles per step
   constexpr int H2 = D / 2;
-  static_assert(CH % NT == 0, "tile must split evenly over the workgroup");
+  static_assert((SPLIT * CH) % NT == 0, "tiles must split evenly over the workgroup");
+  constexpr int NV = D / 32 * 16 + 2;   // merge values per lane: m, l, numerator
+  static_assert(SPLIT == 1 || NW * (SPLIT - 1) * NV * 64 <= 2 * SPLIT * (KT + VT),
+                "merge area must fit in the tile buffers");
 
-  __shared__ __attribute__((aligned(16))) float smem[2 * (KT + VT)];
+  __shared__ __attribute__((aligned(16))) float smem[2 * SPLIT * (KT + VT)];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave_all = tid >> 6;
+  const int grpk = wave_all / NW;          // key group
+  const int wave = wave_all - grpk * NW;   // query wave
   const int lr = lane & 31, hh = lane >> 5;
   const int N = a.N, d = a.d;
 
@@ -87,14 +100,28 @@ void fwd_f32_kernel(FwdArgs a) {
   const int wq_hi = wq_lo + 31;
   const int qi = wq_lo + lr;
 
-  // Q operand: step kk uses feature kk + hh*D/2.
+  // Q operand: step kk uses feature kk + hh*D/2. Every load is unconditional (row and column
+  // clamped into range) so that they are all in flight together; out-of-range values are
+  // replaced by 0 afterwards.
   float qf[H2];
   {
     const float sgn = a.neg ? -1.0f : 1.0f;
+    const bool qv = qi < N;
+    const float* qrow = Qh + (size_t)min(qi, N - 1) * d;
+    if (FULLD) {
 #pragma unroll
-    for (int kk = 0; kk < H2; ++kk) {
-      const int col = kk + hh * H2;
-      qf[kk] = (qi < N && col < d) ? sgn * Qh[(size_t)qi * d + col] : 0.0f;
+      for (int v = 0; v < H2 / 4; ++v) {
+        const f32x4 x = *(const f32x4*)(qrow + hh * H2 + 4 * v);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qf[4 * v + t] = qv ? sgn * x[t] : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < H2; ++kk) {
+        const int col = kk + hh * H2;
+        const float x = qrow[min(col, d - 1)];
+        qf[kk] = (qv && col < d) ? sgn * x : 0.0f;
+      }
     }
   }
 
@@ -109,12 +136,13 @@ void fwd_f32_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
 
   f32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int j) {
-    const int key0 = j * BC;
+  // step `it` stages tiles it*SPLIT .. it*SPLIT + SPLIT-1 (one per key group)
+  auto gload = [&](int it) {
+    const int key0 = it * SPLIT * BC;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + r * NT;
-      const int row = c / (D / 4);
+      const int row = c / (D / 4);      // row within the SPLIT*BC staged keys
       const int col = (c % (D / 4)) * 4;
       const int key = key0 + row;
       f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
@@ -132,40 +160,49 @@ void fwd_f32_kernel(FwdArgs a) {
     }
   };
   auto swrite = [&](int buf) {
-    float* Ks = smem + buf * (KT + VT);
-    float* Vs = Ks + KT;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + r * NT;
       const int row = c / (D / 4);
       const int col = (c % (D / 4)) * 4;
+      float* Ks = smem + (buf * SPLIT + row / BC) * (KT + VT);
+      float* Vs = Ks + KT;
+      const int tr = row % BC;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) Ks[row * KP + col + t] = kreg[r][t];   // odd pitch: scalar stores
-      *(f32x4*)(Vs + row * VP + col) = vreg[r];
+      for (int t = 0; t < 4; ++t) Ks[tr * KP + col + t] = kreg[r][t];   // odd pitch: scalar stores
+      *(f32x4*)(Vs + tr * VP + col) = vreg[r];
     }
   };
 
+  const int nit = (nkv + SPLIT - 1) / SPLIT;   // steps of SPLIT tiles
   gload(0);
   swrite(0);
   __syncthreads();
 
-  for (int j = 0; j < nkv; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkv) gload(j + 1);
-    const float* Ks = smem + buf * (KT + VT);
+  for (int it = 0; it < nit; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nit) gload(it + 1);
+    const float* Ks = smem + (buf * SPLIT + grpk) * (KT + VT);
     const float* Vs = Ks + KT;
+    const int j = it * SPLIT + grpk;   // this key group's tile
     const int key0 = j * BC;
 
-    if (!CAUSAL || key0 <= wq_hi) {
+    if (j < nkv && (!CAUSAL || key0 <= wq_hi)) {
       f32x16 s[BC / 32];
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
         const float* krow = Ks + (kb * 32 + lr) * KP + hh * H2;
+        // all operand reads first, then the MFMA chain (one LDS latency per block, not one
+        // per MFMA)
+        float kop[H2];
+#pragma unroll
+        for (int kk = 0; kk < H2; ++kk) kop[kk] = krow[kk];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < H2; ++kk)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[kk], qf[kk], s[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kop[kk], qf[kk], s[kb], 0, 0, 0);
       }
 
       // Statistics are kept on the unscaled scores: p = 2^((s - m) * sl2). Subtracting
@@ -214,19 +251,60 @@ void fwd_f32_kernel(FwdArgs a) {
       l_run += lsum;
 
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        // operand reads of the whole block first, then the MFMAs
+        float vop[16][D / 32];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
           const float* vrow = Vs + key * VP + lr;
 #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[dt * 32], s[kb][i], acc[dt], 0, 0, 0);
+          for (int dt = 0; dt < D / 32; ++dt) vop[i][dt] = vrow[dt * 32];
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop[i][dt], s[kb][i], acc[dt], 0, 0, 0);
+      }
     }
 
-    if (j + 1 < nkv) swrite(buf ^ 1);
+    if (it + 1 < nit) swrite(buf ^ 1);
     __syncthreads();
+  }
+
+  // ---- merge of the key groups: m* = max m_g, l = sum l_g w_g, u = sum u_g w_g with
+  // w_g = 2^((m_g - m*) * scale * log2 e) (interactiveml.org, merge of the three sufficient
+  // statistics); groups 1.. pass their state to group 0 through LDS.
+  if constexpr (SPLIT > 1) {
+    float* mb = smem;
+    if (grpk > 0) {
+      float* dst = mb + (size_t)((wave * (SPLIT - 1) + grpk - 1) * NV) * 64 + lane;
+      dst[0] = m_run;
+      dst[64] = l_run;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[(2 + dt * 16 + i) * 64] = acc[dt][i];
+    }
+    __syncthreads();
+    if (grpk > 0) return;
+#pragma unroll
+    for (int g = 1; g < SPLIT; ++g) {
+      const float* src = mb + (size_t)((wave * (SPLIT - 1) + g - 1) * NV) * 64 + lane;
+      const float mg = src[0], lg = src[64];
+      const float ms = fmaxf(m_run, mg);
+      // a group that saw no key has m = -inf and weight 0
+      const float w0 = (m_run == -INFINITY) ? 0.0f : exp2f((m_run - ms) * a.sl2);
+      const float wg = (mg == -INFINITY) ? 0.0f : exp2f((mg - ms) * a.sl2);
+      l_run = l_run * w0 + lg * wg;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] = acc[dt][i] * w0 + src[(2 + dt * 16 + i) * 64] * wg;
+      m_run = ms;
+    }
   }
 
   const float l_tot = pair_sum(l_run);
@@ -256,13 +334,28 @@ void fwd_f32_kernel(FwdArgs a) {
   }
 }
 
+template <int D, bool CAUSAL, int SPLIT>
+hipError_t launch_split(const FwdArgs& a, bool fulld, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.BH * a.n_qtiles));
+  const dim3 block(CfgF<D>::NW * SPLIT * 64);
+  if (fulld) hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, true, SPLIT>), grid, block, 0, stream, a);
+  else       hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, false, SPLIT>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// Key groups per workgroup: split the key range while the grid stays small (at most 512
+// workgroups) and every group still gets at least two tiles.
 template <int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.BH * a.n_qtiles));
-  const dim3 block(CfgF<D>::NW * 64);
-  if (fulld) hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, true>), grid, block, 0, stream, a);
-  else       hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, false>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  const long long wgs = (long long)a.BH * a.n_qtiles;
+  const int nkv = (a.N + CfgF<D>::BC - 1) / CfgF<D>::BC;
+  int split = 1;
+  while (split * 2 <= CfgF<D>::MAXSPLIT && wgs * split * 2 <= 512 && nkv >= 2 * split * 2) split *= 2;
+  if constexpr (CfgF<D>::MAXSPLIT >= 4) {
+    if (split == 4) return launch_split<D, CAUSAL, 4>(a, fulld, stream);
+  }
+  if (split == 2) return launch_split<D, CAUSAL, 2>(a, fulld, stream);
+  return launch_split<D, CAUSAL, 1>(a, fulld, stream);
 }
 
 }  // namespace
