@@ -93,6 +93,44 @@ def copy_calibration(mib: int, steps: int) -> None:
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
 
 
+def naive_attention(q, k, v, scale: float, causal: bool, mask=None):
+    """Standard (unfused) attention as the pages describe it before FlashAttention: the N x N
+    score matrix and the probability matrix are both written to and read back from HBM
+    (sadullah.online, "Standard attention"; lihaoran.work, the intermediate matrix).
+    Library GEMMs and a softmax kernel; a comparison only, never the product path."""
+    import torch
+    s = torch.matmul(q, k.transpose(-1, -2).contiguous())   # [B, H, N, N], input dtype
+    s = s.float().mul_(scale)
+    if causal:
+        s.masked_fill_(mask, float("-inf"))
+    p = torch.softmax(s, dim=-1).to(q.dtype)
+    return torch.matmul(p, v)
+
+
+def run_naive(w: inputs.Workload, q, k, v, o_fused, steps: int, warmup: int) -> dict:
+    """Times the unfused comparison on the same device inputs (events over the timed region)."""
+    import torch
+    mask = None
+    if w.causal:
+        mask = torch.ones(w.N, w.N, dtype=torch.bool, device=q.device).triu_(1)
+    scale = w.resolved_scale()
+    for _ in range(warmup):
+        o = naive_attention(q, k, v, scale, w.causal, mask)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        o = naive_attention(q, k, v, scale, w.causal, mask)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t = ev0.elapsed_time(ev1) / steps / 1e3
+    diff = (o.float() - o_fused.float()).abs().max().item()
+    return {"value": round(w.flops / t / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(t * 1e3, 4),
+            "kind": "naive: matmul, softmax, matmul with the N x N matrices in HBM (torch)",
+            "max_abs_diff_vs_fused": diff}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +139,8 @@ def main() -> int:
     ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows per head for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--naive", action="store_true",
+                    help="also time unfused standard attention on the same inputs (comparison)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB --steps times (HBM counter reference)")
     args = ap.parse_args()
@@ -190,6 +230,10 @@ def main() -> int:
                      "kernel_hash": kh},
         "cpu_baseline": None,
     }
+    if args.naive:
+        nv = run_naive(w, q, k, v, o, args.steps, args.warmup)
+        nv["fused_speedup"] = round(nv["ms_per_step"] / (avg_kernel_s * 1e3), 2)
+        line["gpu_naive"] = nv
     if args.cpu_rows > 0:
         line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_rows)
     print(json.dumps(line), flush=True)
