@@ -22,7 +22,7 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
   // element count B*H*N*d must stay below 2^62 (byte offsets then fit in 64 bits)
   const unsigned __int128 count = (unsigned __int128)B * H * N * d;
   if (count > ((unsigned __int128)1 << 62)) return FA_ERR_INVALID_ARG;
-  if (d > 128) return FA_ERR_UNSUPPORTED;
+  if (d > 256) return FA_ERR_UNSUPPORTED;
   // per-head offsets are computed in 64 bits, but row indices and N*d in 32 bits
   if ((int64_t)N * d > INT_MAX) return FA_ERR_UNSUPPORTED;
 
@@ -40,7 +40,7 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
   }
   if (lse != nullptr && overlap(lse, lse_bytes, o, bytes)) return FA_ERR_INVALID_ARG;
 
-  const int dp = d <= 64 ? 64 : 128;
+  const int dp = d <= 64 ? 64 : (d <= 128 ? 128 : 256);
   const int br = rows_per_block(d);
   const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
   if ((int64_t)B * H * n_qtiles > INT_MAX) return FA_ERR_UNSUPPORTED;
@@ -88,7 +88,7 @@ extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
-    case FA_ERR_UNSUPPORTED: return "unsupported problem (head dimension above 128 or problem too large)";
+    case FA_ERR_UNSUPPORTED: return "unsupported problem (head dimension above 256 or problem too large)";
     case FA_ERR_HIP: return "HIP launch error";
     default: return "unknown status";
   }

@@ -100,6 +100,12 @@ template <> struct Cfg<128> {
   static constexpr int QW = FA_BF16_D128_QW, NW = FA_BF16_D128_NW, BC = FA_BF16_D128_BC, WPE = FA_BF16_D128_WPE;
   static constexpr int MAXSPLIT = 1;
 };
+// head widths 129..256: one wave per SIMD (the 256-wide accumulators and operands need more
+// than 256 registers), 4 waves of 32 query rows
+template <> struct Cfg<256> {
+  static constexpr int QW = 1, NW = 4, BC = 32, WPE = 1;
+  static constexpr int MAXSPLIT = 1;
+};
 
 __device__ __forceinline__ float pair_max(float x) {
   // lanes l and l^32 exchange x; after the swap each lane holds both halves' values
@@ -147,17 +153,24 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
   f32x16 s[QW][BC / 32];
 #pragma unroll
   for (int kb = 0; kb < BC / 32; ++kb) {
-    u32x4 kop[D / 16];
+    // (head widths up to 128: all K operands of the block are read before the MFMA chain;
+    // wider heads read them as the chain goes, to bound the registers)
+    constexpr int KOPS = D <= 128 ? D / 16 : 1;
+    u32x4 kop[KOPS];
     const uint16_t* krow = Ks + (kb * 32 + lr) * KP + 8 * hh;
+    if constexpr (D <= 128) {
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) kop[kk] = *(const u32x4*)(krow + 16 * kk);
+      for (int kk = 0; kk < D / 16; ++kk) kop[kk] = *(const u32x4*)(krow + 16 * kk);
+    }
 #pragma unroll
     for (int qb = 0; qb < QW; ++qb) {
       f32x16 c = {};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kop[kk]),
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const u32x4 kv = D <= 128 ? kop[kk % KOPS] : *(const u32x4*)(krow + 16 * kk);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv),
                                                     __builtin_bit_cast(bf16x8, qf[qb][kk]), c, 0, 0, 0);
+      }
       s[qb][kb] = c;
     }
   }
@@ -246,8 +259,12 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
   }
 }
 
+// Minimum waves per SIMD the register allocation must allow: a workgroup of two waves or fewer
+// may use the whole register file (larger ones keep the configured occupancy).
+template <int D, int SPLIT> constexpr int min_waves_per_simd() { return Cfg<D>::NW * SPLIT <= 2 ? 1 : Cfg<D>::WPE; }
+
 template <int D, bool CAUSAL, bool FULLD, int SPLIT>
-__global__ __launch_bounds__(Cfg<D>::NW * SPLIT * 64, Cfg<D>::WPE)
+__global__ __launch_bounds__(Cfg<D>::NW * SPLIT * 64, (min_waves_per_simd<D, SPLIT>()))
 void fwd_bf16_kernel(FwdArgs a) {
   constexpr int QW = Cfg<D>::QW, NW = Cfg<D>::NW, BC = Cfg<D>::BC;
   constexpr int NT = NW * SPLIT * 64;
@@ -517,14 +534,17 @@ hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
 
 int bf16_rows_per_block(int d) {
   if (d == 128) return bf16_d128_rows_per_block();
-  return d <= 64 ? Cfg<64>::NW * Cfg<64>::QW * 32 : Cfg<128>::NW * Cfg<128>::QW * 32;
+  if (d <= 64) return Cfg<64>::NW * Cfg<64>::QW * 32;
+  if (d <= 128) return Cfg<128>::NW * Cfg<128>::QW * 32;
+  return Cfg<256>::NW * Cfg<256>::QW * 32;
 }
 
 hipError_t launch_bf16(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream) {
   if (a.d == 128) return launch_bf16_d128(a, causal, stream);
   const bool fulld = (a.d == d_pad);
   if (d_pad == 64) return causal ? launch_one<64, true>(a, fulld, stream) : launch_one<64, false>(a, fulld, stream);
-  return causal ? launch_one<128, true>(a, fulld, stream) : launch_one<128, false>(a, fulld, stream);
+  if (d_pad == 128) return causal ? launch_one<128, true>(a, fulld, stream) : launch_one<128, false>(a, fulld, stream);
+  return causal ? launch_one<256, true>(a, fulld, stream) : launch_one<256, false>(a, fulld, stream);
 }
 
 }  // namespace fa

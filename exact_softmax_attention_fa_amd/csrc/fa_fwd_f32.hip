@@ -34,7 +34,8 @@ constexpr float kRescaleThreshold = 8.0f;
 // the same queries (taking tiles g, g + SPLIT, ...) and merges them at the end.
 template <int D> struct CfgF;
 template <> struct CfgF<64>  { static constexpr int NW = 1, BC = 32, MAXSPLIT = 4; };
-template <> struct CfgF<128> { static constexpr int NW = 1, BC = 32, MAXSPLIT = 2; };
+template <> struct CfgF<128> { static constexpr int NW = 2, BC = 32, MAXSPLIT = 2; };
+template <> struct CfgF<256> { static constexpr int NW = 4, BC = 32, MAXSPLIT = 1; };
 
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -196,13 +197,17 @@ void fwd_f32_kernel(FwdArgs a) {
         const float* krow = Ks + (kb * 32 + lr) * KP + hh * H2;
         // all operand reads first, then the MFMA chain (one LDS latency per block, not one
         // per MFMA)
-        float kop[H2];
+        // (head widths above 64 read them as the chain goes, to bound the registers)
+        constexpr int KOPS = D <= 64 ? H2 : 1;
+        float kop[KOPS];
+        if constexpr (D <= 64) {
 #pragma unroll
-        for (int kk = 0; kk < H2; ++kk) kop[kk] = krow[kk];
-        __builtin_amdgcn_sched_barrier(0);
+          for (int kk = 0; kk < H2; ++kk) kop[kk] = krow[kk];
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int kk = 0; kk < H2; ++kk)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kop[kk], qf[kk], s[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(D <= 64 ? kop[kk % KOPS] : krow[kk], qf[kk], s[kb], 0, 0, 0);
       }
 
       // Statistics are kept on the unscaled scores: p = 2^((s - m) * sl2). Subtracting
@@ -253,20 +258,27 @@ void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) {
         // operand reads of the whole block first, then the MFMAs
-        float vop[16][D / 32];
+        constexpr int VI = D <= 64 ? 16 : 1;
+        float vop[VI][D / 32];
+        if constexpr (D <= 64) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const float* vrow = Vs + key * VP + lr;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) vop[i][dt] = vrow[dt * 32];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
           const float* vrow = Vs + key * VP + lr;
 #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) vop[i][dt] = vrow[dt * 32];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop[i][dt], s[kb][i], acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(D <= 64 ? vop[i % VI][dt] : vrow[dt * 32], s[kb][i], acc[dt],
+                                                           0, 0, 0);
+        }
       }
     }
 
@@ -354,20 +366,23 @@ hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
   if constexpr (CfgF<D>::MAXSPLIT >= 4) {
     if (split == 4) return launch_split<D, CAUSAL, 4>(a, fulld, stream);
   }
-  if (split == 2) return launch_split<D, CAUSAL, 2>(a, fulld, stream);
+  if constexpr (CfgF<D>::MAXSPLIT >= 2) {
+    if (split == 2) return launch_split<D, CAUSAL, 2>(a, fulld, stream);
+  }
   return launch_split<D, CAUSAL, 1>(a, fulld, stream);
 }
 
 }  // namespace
 
 int f32_rows_per_block(int d) {
-  return d <= 64 ? CfgF<64>::NW * 32 : CfgF<128>::NW * 32;
+  return d <= 64 ? CfgF<64>::NW * 32 : (d <= 128 ? CfgF<128>::NW * 32 : CfgF<256>::NW * 32);
 }
 
 hipError_t launch_f32(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream) {
   const bool fulld = (a.d == d_pad);
   if (d_pad == 64) return causal ? launch_one<64, true>(a, fulld, stream) : launch_one<64, false>(a, fulld, stream);
-  return causal ? launch_one<128, true>(a, fulld, stream) : launch_one<128, false>(a, fulld, stream);
+  if (d_pad == 128) return causal ? launch_one<128, true>(a, fulld, stream) : launch_one<128, false>(a, fulld, stream);
+  return causal ? launch_one<256, true>(a, fulld, stream) : launch_one<256, false>(a, fulld, stream);
 }
 
 }  // namespace fa

@@ -48,7 +48,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null q/k/v/o, B/H/N/d < 1, non-finite or non-positive-size problem,
                               causal not 0/1, element count above 2^62 */
-  FA_ERR_UNSUPPORTED = -2, /* d > 128 (the largest head width compiled), or a grid too large */
+  FA_ERR_UNSUPPORTED = -2, /* d > 256 (the largest head width compiled), or a grid too large */
   FA_ERR_HIP = -3          /* the HIP runtime rejected the launch */
 } fa_status;
 
@@ -60,7 +60,8 @@ typedef enum {
  *   causal  : 0 = all keys, 1 = keys j <= i
  * Arithmetic: fp32 accumulation of both products; the probabilities are rounded to bf16
  * before the product with V; statistics and the normalisation are fp32.
- * Supported: 1 <= d <= 128 (d = 64 and d = 128 are the tuned widths), any N >= 1. */
+ * Supported: 1 <= d <= 256 (d = 64 and d = 128 are the tuned widths; other widths run on the
+ * kernel for the next width up of 64, 128 or 256), any N >= 1. */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 

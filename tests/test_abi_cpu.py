@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     assert fa.fa_status_string(fa.FA_OK) == "ok"
     assert fa.fa_status_string(fa.FA_ERR_INVALID_ARG) == "invalid argument"
-    assert "128" in fa.fa_status_string(fa.FA_ERR_UNSUPPORTED)
+    assert "256" in fa.fa_status_string(fa.FA_ERR_UNSUPPORTED)
     assert fa.fa_status_string(fa.FA_ERR_HIP) == "HIP launch error"
     assert fa.fa_status_string(12345) == "unknown status"
 
@@ -71,7 +71,7 @@ def call(fn, q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=16, d=64, scale=0.125, causa
     (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
-    (dict(d=129), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=257), fa.FA_ERR_UNSUPPORTED),
     (dict(d=4096), fa.FA_ERR_UNSUPPORTED),
     (dict(B=2 ** 31 - 1, H=2 ** 31 - 1, N=2 ** 31 - 1, d=128), fa.FA_ERR_INVALID_ARG),   # > 2^62 elements
     (dict(N=2 ** 25, d=128), fa.FA_ERR_UNSUPPORTED),                                 # N*d above 2^31

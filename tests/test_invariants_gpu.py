@@ -93,8 +93,8 @@ def test_non_default_stream():
 
 def test_errors_on_device():
     import torch
-    q = torch.zeros((1, 1, 8, 256), dtype=torch.bfloat16, device="cuda")
-    note("unsupported head width")
+    q = torch.zeros((1, 1, 8, 320), dtype=torch.bfloat16, device="cuda")
+    note("unsupported head width (above 256)")
     with pytest.raises(fa.FaError) as e:
         fa.fwd(q, q.clone(), q.clone())
     assert e.value.status == fa.FA_ERR_UNSUPPORTED

@@ -117,6 +117,34 @@ def test_f32_shapes(N, d, causal):
     full_parity(t, "f32", 1 / math.sqrt(d), causal, f"f32 N{N} d{d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [129, 160, 200, 256])
+@pytest.mark.parametrize("N", [33, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_wide_heads(d, N, causal):
+    """Head widths above 128 run on the 256-wide kernel (masked loads below 256)."""
+    t = inputs.make_random(1, 2, N, d, "bf16", seed=1100 + N + d)
+    full_parity(t, "bf16", 1 / math.sqrt(d), causal, f"bf16 N{N} d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [160, 256])
+@pytest.mark.parametrize("N", [33, 200])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_wide_heads(d, N, causal):
+    t = inputs.make_random(1, 2, N, d, "f32", seed=1200 + N + d)
+    full_parity(t, "f32", 1 / math.sqrt(d), causal, f"f32 N{N} d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype,d,N,BH", [("bf16", 64, 1000, 1), ("bf16", 40, 600, 2), ("bf16", 64, 300, 3),
+                                          ("f32", 64, 256, 1), ("f32", 64, 100, 1), ("f32", 100, 200, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_split_groups(dtype, d, N, BH, causal):
+    """Small grids split the key range over up to 4 groups of waves in a workgroup and merge
+    their statistics (these shapes give splits of 2 and 4, with groups that see no key on the
+    first causal query tiles and a ragged last tile)."""
+    t = inputs.make_random(1, BH, N, d, dtype, seed=1300 + N + d + BH)
+    full_parity(t, dtype, 1 / math.sqrt(d), causal, f"{dtype} split N{N} d{d} BH{BH} causal={causal}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
 def test_other_scales(dtype, scale):
