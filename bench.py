@@ -31,22 +31,31 @@ from exact_softmax_attention_fa_amd import inputs  # noqa: E402
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
-KERNEL_SOURCES = ["exact_softmax_attention_fa_amd/csrc/fa_fwd_bf16.hip",
-                  "exact_softmax_attention_fa_amd/csrc/fa_fwd_bf16_d128.hip",
-                  "exact_softmax_attention_fa_amd/csrc/fa_fwd_f32.hip",
-                  "exact_softmax_attention_fa_amd/csrc/fa_internal.h"]
+CSRC = "exact_softmax_attention_fa_amd/csrc/"
+
+
+def kernel_sources(w: inputs.Workload) -> list:
+    """Sources of the kernel a workload runs (the key under which its traffic is stored)."""
+    if w.dtype == "f32":
+        main = "fa_fwd_f32.hip"
+    elif w.d == 128:
+        main = "fa_fwd_bf16_d128.hip"
+    else:
+        main = "fa_fwd_bf16.hip"
+    return [CSRC + main, CSRC + "fa_internal.h"]
+
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
 # dispatch), each scaled by the factor the same counter reads for a plain copy of known size.
 # Keyed by workload; valid only for the kernel sources whose hash is stored with them.
 TRAFFIC = {
-    "fwd_bf16_b1_h16_n8192_d128_widek": {"bytes": 202242874, "kernel_hash": "c80571c7b3099573"},
+    "fwd_bf16_b1_h16_n8192_d128_widek": {"bytes": 202242874, "kernel_hash": "b1e5c5614a7fb3af"},
 }
 
 
-def kernel_hash() -> str:
+def kernel_hash(w: inputs.Workload) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in kernel_sources(w):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -201,7 +210,7 @@ def main() -> int:
     tflops = w.flops / (wall / args.steps) / 1e12
     achieved = w.flops / avg_kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    kh = kernel_hash()
+    kh = kernel_hash(w)
     traffic = TRAFFIC.get(w.name)
     traffic_bytes = traffic["bytes"] if traffic and traffic.get("kernel_hash") == kh else None
 
