@@ -7,4 +7,4 @@ with the HIP path.
 Every function is pinned by tests/test_oracle_pins.py to values and properties the
 pages and the mathematics fix; no function here is left "parity unpinned".
 """
-from . import attention, online  # noqa: F401  (modules; call attention.attention(...))
+from . import attention, backward, online  # noqa: F401  (modules; call attention.attention(...))
