@@ -19,8 +19,8 @@ O = P V, and dO the gradient of a scalar loss with respect to O, per (b, h):
     dK = scale * dS^T Q
 
 Everything is float64 and P is materialised one block of query rows at a time.
-Parity pins: tests/test_oracle_pins.py (central finite differences on tiny inputs,
-torch's float64 autograd, closed forms for special inputs, invariants).
+Parity pins: tests/oracle_bwd_pins.py (central finite differences on tiny inputs, a library
+autograd routine in float64, closed forms for special inputs, invariants).
 """
 from __future__ import annotations
 
