@@ -140,6 +140,46 @@ def run_naive(w: inputs.Workload, q, k, v, o_fused, steps: int, warmup: int) -> 
             "max_abs_diff_vs_fused": diff}
 
 
+def run_backward(w: inputs.Workload, q, k, v, o, lse, steps: int, warmup: int) -> dict:
+    """Times fa_bwd (delta, dK/dV and dQ kernels) on the forward's own outputs; a seeded
+    bf16 N(0,1) output gradient. Events on the launch stream over the timed region."""
+    import numpy as np
+    import torch
+    import exact_softmax_attention_fa_amd as fa
+    if w.dtype != "bf16" or w.d not in (64, 128):
+        return {"skipped": "the backward pass supports bf16 with d = 64 or 128"}
+    g = inputs.make_backward(w.B, w.H, w.N, w.d, w.seed + 100)["dout"]
+    dout = torch.from_numpy(np.ascontiguousarray(g).view(np.int16)).view(torch.bfloat16).to(q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), w.B, w.H, w.N, w.d,
+            w.resolved_scale(), 1 if w.causal else 0, stream.cuda_stream)
+
+    def call():
+        st = fa.fa_bwd(*args)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, "fa_bwd")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t = ev0.elapsed_time(ev1) / steps / 1e3
+    flops = 2.5 * w.flops   # five N^2 d products per head against the forward's two
+    return {"value": round(flops / t / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(t * 1e3, 4),
+            "algorithmic_flops_per_call": flops,
+            "note": "flops counted as 2.5x the forward (S recomputed once); the kernels compute S and dP "
+                    "twice (dK/dV pass and dQ pass), 3.5x the forward's products",
+            "pct_of_peak": round(100.0 * flops / t / 1e12 / PEAK_TFLOPS[w.dtype], 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +188,8 @@ def main() -> int:
     ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows per head for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward pass (fa_bwd) on the forward's outputs")
     ap.add_argument("--naive", action="store_true",
                     help="also time unfused standard attention on the same inputs (comparison)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -239,6 +281,8 @@ def main() -> int:
                      "kernel_hash": kh},
         "cpu_baseline": None,
     }
+    if args.backward:
+        line["backward"] = run_backward(w, q, k, v, o, lse, args.steps, args.warmup)
     if args.naive:
         nv = run_naive(w, q, k, v, o, args.steps, args.warmup)
         nv["fused_speedup"] = round(nv["ms_per_step"] / (avg_kernel_s * 1e3), 2)

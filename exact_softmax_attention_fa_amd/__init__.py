@@ -7,9 +7,11 @@ kernels. PyTorch supplies device memory and the stream.
 Entry points with the C names:
   fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> status   (bf16, raw pointers)
   fa_fwd_f32(...)                                              -> status   (fp32, raw pointers)
+  fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream) -> status
   fa_status_string(status)                                     -> str
-and a tensor-level convenience:
+and tensor-level conveniences:
   fwd(q, k, v, scale=None, causal=False) -> (o, lse)
+  bwd(q, k, v, o, lse, dout, scale=None, causal=False) -> (dq, dk, dv)
 If the library has not been built, every call raises RuntimeError; there is no fallback.
 """
 from __future__ import annotations
@@ -18,7 +20,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_status_string", "fwd", "library_path", "load_library",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_status_string", "fwd", "bwd", "library_path", "load_library",
            "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FaError"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
@@ -54,6 +56,9 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = argtypes
         fn.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                                          ctypes.c_void_p]
+    lib.fa_bwd.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -68,6 +73,11 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
 def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
     """fp32 forward on raw device pointers (ints); returns the C status code."""
     return load_library().fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream) -> int:
+    """bf16 backward on raw device pointers (ints); returns the C status code."""
+    return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -116,3 +126,33 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
     if st != FA_OK:
         raise FaError(st, fn.__name__)
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False, stream=None):
+    """Gradients (dq, dk, dv) of attention on bf16 torch tensors [B, H, N, d] (d = 64 or 128).
+
+    ``o`` and ``lse`` are the forward's outputs for the same inputs, ``dout`` the gradient of
+    the loss with respect to ``o``. Allocates the outputs and the fp32 [B, H, N] workspace with
+    torch and enqueues the work on ``stream`` (default: the current stream) without waiting.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor shaped like q on q's device")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B,H,N] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, float(scale),
+                1 if causal else 0, handle)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -84,6 +84,57 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
   return fa::launch_f32(args, d_pad, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                      int d, float scale, int causal, hipStream_t stream) {
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  void* outs[4] = {dq, dk, dv, delta};
+  for (const void* p : ins) if (p == nullptr) return FA_ERR_INVALID_ARG;
+  for (const void* p : outs) if (p == nullptr) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  const unsigned __int128 count = (unsigned __int128)B * H * N * d;
+  if (count > ((unsigned __int128)1 << 62)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)N * d > INT_MAX) return FA_ERR_UNSUPPORTED;
+  const int64_t nblk = ((int64_t)N + fa::bwd_rows_per_block() - 1) / fa::bwd_rows_per_block();
+  if ((int64_t)B * H * nblk > INT_MAX) return FA_ERR_UNSUPPORTED;
+
+  // no output may overlap an input or another output
+  const uint64_t tb = (uint64_t)count * 2, rb = (uint64_t)B * H * N * sizeof(float);
+  const uint64_t in_bytes[6] = {tb, tb, tb, tb, tb, rb};
+  const uint64_t out_bytes[4] = {tb, tb, tb, rb};
+  auto overlap = [](const void* x, uint64_t nx, const void* y, uint64_t ny) {
+    const uintptr_t a0 = (uintptr_t)x, b0 = (uintptr_t)y;
+    return a0 < b0 + ny && b0 < a0 + nx;
+  };
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_INVALID_ARG;
+  }
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = delta;
+  a.N = N;
+  a.d = d;
+  a.BH = B * H;
+  a.sl2 = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
+  a.neg = scale < 0.0f ? 1 : 0;
+  return fa::launch_bwd_bf16(a, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

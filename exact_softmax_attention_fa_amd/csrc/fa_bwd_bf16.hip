@@ -1,0 +1,461 @@
+// Backward pass of exact softmax attention, bf16 inputs, for gfx950 (CDNA4).
+//
+// The probabilities are recomputed from q, k and the forward's saved log-normaliser instead
+// of being stored (lihaoran.work, "The intermediate matrix comes first": FlashAttention
+// recomputes in the backward pass). The gradients are those of the definition O = P V,
+// P = softmax(scale Q K^T) row by row:
+//   delta_i = sum_c dO_ic O_ic                 (= sum_k P_ik dP_ik)
+//   P_ij    = exp(scale q_i.k_j - lse_i)       (0 where masked)
+//   dP_ij   = dO_i . v_j
+//   dS_ij   = P_ij (dP_ij - delta_i)
+//   dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K
+//
+// Three kernels, no atomics:
+// * bwd_delta_kernel: delta per row (fp32), into the caller's workspace.
+// * bwd_dkdv_kernel: a workgroup owns 128 keys (4 waves x 32); it walks the query blocks of
+//   32 rows, staged through LDS (Q, dO, log-normaliser, delta). Per block and wave:
+//     S = Q K^T and dP = dO V^T with K and V held in registers as B operands, so that the
+//     accumulator holds one key per lane and 16 queries in its registers;
+//     dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by
+//     ds_read_b64_tr_b16 from the row-major Q and dO tiles, and P / dS taken from the
+//     accumulator registers as the B operands (the same register/key correspondence as the
+//     forward kernels, with the roles of queries and keys exchanged).
+// * bwd_dq_kernel: a workgroup owns 128 queries (4 waves x 32) and walks the key tiles of
+//   32, like the forward: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then
+//   dQ^T += K^T dS^T with K^T read transposed from the K tile.
+// Scores stay in base-2 units (|scale| log2 e folded into one multiply); a negative scale
+// negates q exactly and dQ at the end. P and dS are rounded to bf16 for the MFMAs, with fp32
+// accumulation; the outputs are rounded to bf16 once.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int NW = 4;        // waves per workgroup
+constexpr int NT = NW * 64;
+constexpr int BLK = 32;      // rows per MFMA block (keys or queries)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// MFMA 32x32x16 bf16 with fp32 accumulation
+__device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Transposed operand from a row-major [row][feature] LDS tile (pitch P elements): lane l gets
+// feature 32*dt + l%32 for rows 16*c16 + {4hh + r, 8 + 4hh + r} (r = 0..3), the order in
+// which the accumulator registers 8c..8c+7 hold their rows.
+template <int P>
+__device__ __forceinline__ u32x4 read_tr(const uint16_t* tile, int c16, int dt, int tr_row, int tr_col) {
+  const uint16_t* base = tile + (c16 * 16 + tr_row) * P + dt * 32 + tr_col;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * P));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+  return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
+}
+
+// ---- delta_i = sum_c dO_ic O_ic ------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256)
+void bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, float* __restrict__ delta,
+                      long long rows) {
+  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const u32x4* orow = (const u32x4*)(o + r * D);
+  const u32x4* drow = (const u32x4*)(dout + r * D);
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4 x = orow[c], y = drow[c];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s0 = fmaf(bf16_lo(x[t]), bf16_lo(y[t]), s0);
+      s1 = fmaf(bf16_hi(x[t]), bf16_hi(y[t]), s1);
+    }
+  }
+  delta[r] = s0 + s1;
+}
+
+// ---- dK, dV --------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, 1)
+void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int QP = D + 16;            // Q / dO tile pitch (transpose reads conflict-free)
+  constexpr int QT = BLK * QP;
+  constexpr int STAGE = 2 * QT;         // Q tile, dO tile (elements)
+  constexpr int CH = BLK * D / 8;       // 16-byte chunks per tile
+  static_assert(CH % NT == 0 || NT % CH == 0, "tile split");
+  constexpr int CPT = (2 * CH + NT - 1) / NT;   // chunks per thread (Q and dO)
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float sstat[2][2][BLK];   // [buf][lse2, delta][row]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, hh = lane >> 5;
+  const int N = a.N;
+  const float sl2 = a.sl2;
+  const uint32_t negmask = a.neg ? 0x80008000u : 0u;
+
+  // heads vary fastest; under a causal mask the first key blocks see the most queries, so
+  // the dispatch order is already heaviest first
+  const int id = blockIdx.x;
+  const int kblk = id / a.BH;
+  const int bh = id - kblk * a.BH;
+  const int k0 = kblk * NW * BLK;
+  const int kw0 = k0 + wave * BLK;      // this wave's first key
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* __restrict__ Qh = (const uint16_t*)a.q + head;
+  const uint16_t* __restrict__ Kh = (const uint16_t*)a.k + head;
+  const uint16_t* __restrict__ Vh = (const uint16_t*)a.v + head;
+  const uint16_t* __restrict__ dOh = (const uint16_t*)a.dout + head;
+  const float* __restrict__ lseh = a.lse + (size_t)bh * N;
+  const float* __restrict__ delh = a.delta + (size_t)bh * N;
+
+  // K^T and V^T as B operands: lane l supplies key kw0 + l%32, features 16kk + 8hh .. +7
+  const int key = kw0 + lr;
+  u32x4 kf[D / 16], vf[D / 16];
+  {
+    const uint32_t keep = key < N ? 0xffffffffu : 0u;
+    const uint16_t* krow = Kh + (size_t)min(key, N - 1) * D;
+    const uint16_t* vrow = Vh + (size_t)min(key, N - 1) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kf[kk] = *(const u32x4*)(krow + 16 * kk + 8 * hh) & keep;
+      vf[kk] = *(const u32x4*)(vrow + 16 * kk + 8 * hh) & keep;
+    }
+  }
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
+
+  // query blocks: causal ones start at the first block that holds a query >= k0
+  const int nqb = (N + BLK - 1) / BLK;
+  const int qb0 = CAUSAL ? k0 / BLK : 0;
+
+  // staging: chunk c < CH is Q, CH <= c < 2CH is dO; row c/(D/8) of the block, 8 features
+  u32x4 sreg[CPT];
+  float st_lse = 0.0f, st_del = 0.0f;
+  auto gload = [&](int qb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + r * NT;
+      if (c < 2 * CH) {
+        const int cc = c % CH;
+        const int row = qb * BLK + cc / (D / 8);
+        const int col = (cc % (D / 8)) * 8;
+        const uint16_t* src = c < CH ? Qh : dOh;
+        const uint32_t keep = row < N ? 0xffffffffu : 0u;
+        u32x4 x = *(const u32x4*)(src + (size_t)min(row, N - 1) * D + col) & keep;
+        if (c < CH) x ^= (negmask & keep);
+        sreg[r] = x;
+      }
+    }
+    if (tid < BLK) {
+      const int row = min(qb * BLK + tid, N - 1);
+      st_lse = lseh[row] * kLog2e;
+      st_del = delh[row];
+    }
+  };
+  auto swrite = [&](int buf) __attribute__((always_inline)) {
+    uint16_t* base = smem + buf * STAGE;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + r * NT;
+      if (c < 2 * CH) {
+        const int cc = c % CH;
+        const int row = cc / (D / 8);
+        const int col = (cc % (D / 8)) * 8;
+        *(u32x4*)(base + (c < CH ? 0 : QT) + row * QP + col) = sreg[r];
+      }
+    }
+    if (tid < BLK) {
+      sstat[buf][0][tid] = st_lse;
+      sstat[buf][1][tid] = st_del;
+    }
+  };
+
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  if (qb0 < nqb) {
+    gload(qb0);
+    swrite(0);
+  }
+  __syncthreads();
+  for (int qb = qb0; qb < nqb; ++qb) {
+    const int buf = (qb - qb0) & 1;
+    if (qb + 1 < nqb) gload(qb + 1);
+    const uint16_t* Qs = smem + buf * STAGE;
+    const uint16_t* dOs = Qs + QT;
+    const int qf0 = qb * BLK;   // first query of the block
+    // skip blocks whose queries all precede this wave's keys (causal), and waves past N
+    if ((!CAUSAL || qf0 + BLK - 1 >= kw0) && kw0 < N) {
+      // S = Q K^T, dP = dO V^T: lane = key, register i = query 8(i/4) + 4hh + i%4
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const u32x4 qa = *(const u32x4*)(Qs + lr * QP + 16 * kk + 8 * hh);
+        const u32x4 da = *(const u32x4*)(dOs + lr * QP + 16 * kk + 8 * hh);
+        s = mfma(qa, kf[kk], s);
+        dp = mfma(da, vf[kk], dp);
+      }
+      const bool masked = (qf0 + BLK > N) || (kw0 + BLK > N) || (CAUSAL && qf0 < kw0 + BLK - 1);
+      u32x4 pb[2], db[2];
+      float p[16], ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *(const f32x4*)(&sstat[buf][0][8 * g + 4 * hh]);
+        const f32x4 d4 = *(const f32x4*)(&sstat[buf][1][8 * g + 4 * hh]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int i = 4 * g + t;
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -l4[t]));
+          if (masked) {
+            const int qi = qf0 + 8 * g + 4 * hh + t;
+            if (qi >= N || key >= N || (CAUSAL && key > qi)) pv = 0.0f;
+          }
+          p[i] = pv;
+          ds[i] = pv * (dp[i] - d4[t]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        pb[c] = (u32x4){pack_bf16x2(p[8 * c + 0], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
+                        pack_bf16x2(p[8 * c + 4], p[8 * c + 5]), pack_bf16x2(p[8 * c + 6], p[8 * c + 7])};
+        db[c] = (u32x4){pack_bf16x2(ds[8 * c + 0], ds[8 * c + 1]), pack_bf16x2(ds[8 * c + 2], ds[8 * c + 3]),
+                        pack_bf16x2(ds[8 * c + 4], ds[8 * c + 5]), pack_bf16x2(ds[8 * c + 6], ds[8 * c + 7])};
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query chunks
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          dv[dt] = mfma(read_tr<QP>(dOs, c, dt, tr_row, tr_col), pb[c], dv[dt]);
+          dk[dt] = mfma(read_tr<QP>(Qs, c, dt, tr_row, tr_col), db[c], dk[dt]);
+        }
+    }
+    if (qb + 1 < nqb) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dK = |scale| * (Q'^T dS)^T, dV as accumulated; lane = key, registers = features
+  if (key < N) {
+    const float kscale = sl2 / kLog2e;
+    uint16_t* dkrow = (uint16_t*)a.dk + head + (size_t)key * D;
+    uint16_t* dvrow = (uint16_t*)a.dv + head + (size_t)key * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = dt * 32 + 8 * g + 4 * hh;
+        const u32x2 wk = {pack_bf16x2(dk[dt][4 * g + 0] * kscale, dk[dt][4 * g + 1] * kscale),
+                          pack_bf16x2(dk[dt][4 * g + 2] * kscale, dk[dt][4 * g + 3] * kscale)};
+        const u32x2 wv = {pack_bf16x2(dv[dt][4 * g + 0], dv[dt][4 * g + 1]),
+                          pack_bf16x2(dv[dt][4 * g + 2], dv[dt][4 * g + 3])};
+        *(u32x2*)(dkrow + col) = wk;
+        *(u32x2*)(dvrow + col) = wv;
+      }
+  }
+}
+
+// ---- dQ ------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, 2)
+void bwd_dq_kernel(BwdArgs a) {
+  constexpr int KP = D + 16;            // K tile pitch (row reads and transpose reads)
+  constexpr int VP = D + 8;             // V tile pitch (row reads)
+  constexpr int KT = BLK * KP, VT = BLK * VP;
+  constexpr int STAGE = KT + VT;
+  constexpr int CH = BLK * D / 8;
+  constexpr int CPT = (2 * CH + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, hh = lane >> 5;
+  const int N = a.N;
+  const float sl2 = a.sl2;
+  const uint32_t negmask = a.neg ? 0x80008000u : 0u;
+
+  const int nqt = (N + NW * BLK - 1) / (NW * BLK);
+  const int id = blockIdx.x;
+  const int qt_rev = id / a.BH;
+  const int bh = id - qt_rev * a.BH;
+  const int qt = CAUSAL ? (nqt - 1 - qt_rev) : qt_rev;   // causal: heaviest first
+  const int q0 = qt * NW * BLK;
+  const int qw0 = q0 + wave * BLK;
+  const int qi = qw0 + lr;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* __restrict__ Qh = (const uint16_t*)a.q + head;
+  const uint16_t* __restrict__ Kh = (const uint16_t*)a.k + head;
+  const uint16_t* __restrict__ Vh = (const uint16_t*)a.v + head;
+  const uint16_t* __restrict__ dOh = (const uint16_t*)a.dout + head;
+
+  // Q'^T and dO^T as B operands (lane = query)
+  u32x4 qf[D / 16], df[D / 16];
+  const uint32_t keep = qi < N ? 0xffffffffu : 0u;
+  {
+    const uint16_t* qrow = Qh + (size_t)min(qi, N - 1) * D;
+    const uint16_t* drow = dOh + (size_t)min(qi, N - 1) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = (*(const u32x4*)(qrow + 16 * kk + 8 * hh) & keep) ^ negmask;
+      df[kk] = *(const u32x4*)(drow + 16 * kk + 8 * hh) & keep;
+    }
+  }
+  const float lse2 = a.lse[(size_t)bh * N + min(qi, N - 1)] * kLog2e;
+  const float dlt = a.delta[(size_t)bh * N + min(qi, N - 1)];
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[dt][i] = 0.0f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + NW * BLK) : N;
+  const int nkt = (kv_end + BLK - 1) / BLK;
+
+  u32x4 sreg[CPT];
+  auto gload = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + r * NT;
+      if (c < 2 * CH) {
+        const int cc = c % CH;
+        const int row = t * BLK + cc / (D / 8);
+        const int col = (cc % (D / 8)) * 8;
+        const uint16_t* src = c < CH ? Kh : Vh;
+        const uint32_t kp = row < N ? 0xffffffffu : 0u;
+        sreg[r] = *(const u32x4*)(src + (size_t)min(row, N - 1) * D + col) & kp;
+      }
+    }
+  };
+  auto swrite = [&](int buf) __attribute__((always_inline)) {
+    uint16_t* base = smem + buf * STAGE;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+      const int c = tid + r * NT;
+      if (c < 2 * CH) {
+        const int cc = c % CH;
+        const int row = cc / (D / 8);
+        const int col = (cc % (D / 8)) * 8;
+        if (c < CH) *(u32x4*)(base + row * KP + col) = sreg[r];
+        else *(u32x4*)(base + KT + row * VP + col) = sreg[r];
+      }
+    }
+  };
+
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+  for (int t = 0; t < nkt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nkt) gload(t + 1);
+    const uint16_t* Ks = smem + buf * STAGE;
+    const uint16_t* Vs = Ks + KT;
+    const int key0 = t * BLK;
+    if ((!CAUSAL || key0 <= qw0 + BLK - 1) && qw0 < N) {
+      // S^T = K Q'^T, dP^T = V dO^T: lane = query, register i = key 8(i/4) + 4hh + i%4
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const u32x4 ka = *(const u32x4*)(Ks + lr * KP + 16 * kk + 8 * hh);
+        const u32x4 va = *(const u32x4*)(Vs + lr * VP + 16 * kk + 8 * hh);
+        s = mfma(ka, qf[kk], s);
+        dp = mfma(va, df[kk], dp);
+      }
+      const bool masked = (key0 + BLK > N) || (qi >= N) || (CAUSAL && key0 + BLK - 1 > qw0);
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2));
+        if (masked) {
+          const int kj = key0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (kj >= N || qi >= N || (CAUSAL && kj > qi)) pv = 0.0f;
+        }
+        ds[i] = pv * (dp[i] - dlt);
+      }
+      u32x4 db[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        db[c] = (u32x4){pack_bf16x2(ds[8 * c + 0], ds[8 * c + 1]), pack_bf16x2(ds[8 * c + 2], ds[8 * c + 3]),
+                        pack_bf16x2(ds[8 * c + 4], ds[8 * c + 5]), pack_bf16x2(ds[8 * c + 6], ds[8 * c + 7])};
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) dq[dt] = mfma(read_tr<KP>(Ks, c, dt, tr_row, tr_col), db[c], dq[dt]);
+    }
+    if (t + 1 < nkt) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ = scale * (dS K): |scale| from the accumulation, sign from the flipped q
+  if (qi < N) {
+    const float qscale = (a.neg ? -1.0f : 1.0f) * (sl2 / kLog2e);
+    uint16_t* dqrow = (uint16_t*)a.dq + head + (size_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = dt * 32 + 8 * g + 4 * hh;
+        const u32x2 w = {pack_bf16x2(dq[dt][4 * g + 0] * qscale, dq[dt][4 * g + 1] * qscale),
+                         pack_bf16x2(dq[dt][4 * g + 2] * qscale, dq[dt][4 * g + 3] * qscale)};
+        *(u32x2*)(dqrow + col) = w;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+  const long long rows = (long long)a.BH * a.N;
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                     (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
+  const unsigned nblk = (unsigned)((a.N + NW * BLK - 1) / (NW * BLK));
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int bwd_rows_per_block() { return NW * BLK; }
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.d == 64) return causal ? launch_bwd_d<64, true>(a, stream) : launch_bwd_d<64, false>(a, stream);
+  return causal ? launch_bwd_d<128, true>(a, stream) : launch_bwd_d<128, false>(a, stream);
+}
+
+}  // namespace fa

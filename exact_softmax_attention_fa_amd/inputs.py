@@ -145,6 +145,13 @@ def make_random(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     return {"q": _store(q, dtype), "k": _store(k, dtype), "v": _store(v, dtype)}
 
 
+def make_backward(B: int, H: int, N: int, d: int, seed: int) -> dict:
+    """Seeded bf16 q, k, v and an output gradient dout, all iid N(0,1) (backward checks)."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    return {x: _store(rng.standard_normal(shape), "bf16") for x in ("q", "k", "v", "dout")}
+
+
 def scalar_case(scores, values) -> dict:
     """Express a one-query scalar example through the [B,H,N,d] interface.
 

@@ -70,6 +70,24 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
+/* Backward pass, bf16 (recomputes the probabilities from q, k and lse instead of storing
+ * them: lihaoran.work, "The intermediate matrix comes first"; the gradients are those of the
+ * definition O = softmax(scale q k^T [masked]) v).
+ *   q, k, v : the forward's inputs, device bf16 [B][H][N][d], read only
+ *   o, lse  : the forward's outputs for the same q, k, v, scale, causal: o bf16 [B][H][N][d],
+ *             lse fp32 [B][H][N] (natural-log normaliser, as fa_fwd writes it), read only
+ *   dout    : gradient of the loss with respect to o, device bf16 [B][H][N][d], read only
+ *   dq, dk, dv : gradients with respect to q, k, v, device bf16 [B][H][N][d], written
+ *   delta   : device fp32 workspace of B*H*N floats, written (row sums of dout * o); owned by
+ *             the caller, no allocation happens inside
+ * Arithmetic: fp32 accumulation; the probabilities and their gradients are rounded to bf16
+ * before the matrix products. No output may overlap an input or another output.
+ * Supported: d = 64 or 128, any N >= 1; other widths return FA_ERR_UNSUPPORTED. Asynchronous
+ * on `stream` like fa_fwd; the same error rules apply. */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, float* delta,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);
 

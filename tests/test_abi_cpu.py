@@ -28,7 +28,7 @@ def lib():
 
 
 def test_header_declares_entry_points():
-    assert header_functions() == ["fa_fwd", "fa_fwd_f32", "fa_status_string"]
+    assert header_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -81,6 +81,34 @@ def call(fn, q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=16, d=64, scale=0.125, causa
 ])
 def test_invalid_arguments_rejected_on_host(lib, fn, kwargs, status):
     assert call(fn, **kwargs) == status
+
+
+DO, DQ, DK, DV, DL = 6 * BIG, 7 * BIG, 8 * BIG, 9 * BIG, 10 * BIG
+
+
+def call_bwd(q=Q, k=K, v=V, o=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=1, N=16, d=64,
+             scale=0.125, causal=0):
+    return fa.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dout=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=None), fa.FA_ERR_INVALID_ARG),
+    (dict(delta=None), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dq=Q + 64), fa.FA_ERR_INVALID_ARG),       # dq overlaps q
+    (dict(dk=DQ + 2), fa.FA_ERR_INVALID_ARG),       # dk overlaps dq
+    (dict(delta=DO + 8), fa.FA_ERR_INVALID_ARG),    # workspace overlaps dout
+    (dict(dv=L + 4), fa.FA_ERR_INVALID_ARG),        # dv overlaps lse
+])
+def test_backward_invalid_arguments_rejected_on_host(lib, kwargs, status):
+    assert call_bwd(**kwargs) == status
 
 
 def test_missing_library_fails_loudly(tmp_path):

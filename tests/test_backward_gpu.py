@@ -1,0 +1,81 @@
+"""Backward pass on the GPU (fa_bwd through the C-ABI) against the fp64 oracle's gradients.
+
+Inputs q, k, v, dout are seeded bf16 draws. The forward outputs o and lse that fa_bwd takes
+come either from the oracle (rounded to the storage formats: o to bf16, lse to fp32) or
+from fa_fwd itself (the end-to-end use); the oracle's gradients are always computed from
+q, k, v, dout alone."""
+import math
+
+import numpy as np
+import pytest
+
+from exact_softmax_attention_fa_amd import inputs
+from gpu_util import note, to_device
+from oracle import attention as oracle
+from oracle import backward as oracle_bwd
+
+pytestmark = pytest.mark.gpu
+
+# Tolerance per gradient tensor g (derived in the design notes from the bf16 roundings of o,
+# P and dS): max |g_gpu - g_ref| <= 2^-6 * max(1, max |g_ref|) and
+# mean |g_gpu - g_ref| <= 2^-9 * max(1, max |g_ref|).
+def check(g_gpu, g_ref, label):
+    scale = max(1.0, float(np.abs(g_ref).max()))
+    err = np.abs(g_gpu - g_ref)
+    assert np.all(np.isfinite(g_gpu)), f"{label}: non-finite gradient"
+    mx, mn = float(err.max()) / scale, float(err.mean()) / scale
+    assert mx <= 2.0 ** -6, f"{label}: max abs error {mx:.3e} x {scale:.3g} above 2^-6"
+    assert mn <= 2.0 ** -9, f"{label}: mean abs error {mn:.3e} x {scale:.3g} above 2^-9"
+    return mx, mn
+
+
+def run_case(B, H, N, d, causal, seed, scale=None, forward="oracle"):
+    import torch
+    import exact_softmax_attention_fa_amd as fa
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    t = inputs.make_backward(B, H, N, d, seed)
+    q64, k64, v64, do64 = (oracle.as_fp64(t[x], "bf16") for x in ("q", "k", "v", "dout"))
+    dq_r, dk_r, dv_r = oracle_bwd.gradients(q64, k64, v64, do64, scale, causal)
+    q, k, v, dout = (to_device(t[x], "bf16") for x in ("q", "k", "v", "dout"))
+    note(f"backward B{B} H{H} N{N} d{d} causal={causal} scale={scale:.4g} forward={forward}")
+    if forward == "oracle":
+        o_ref, lse_ref = oracle.attention(q64, k64, v64, scale, causal)
+        o = to_device(inputs.f32_to_bf16_bits(o_ref.astype(np.float32)), "bf16")
+        lse = torch.from_numpy(lse_ref.astype(np.float32)).cuda()
+    else:
+        o, lse = fa.fwd(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, dout, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    out = {}
+    for name, g, r in (("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r)):
+        out[name] = check(g.double().cpu().numpy(), r, f"{name} B{B} H{H} N{N} d{d} causal={causal}")
+    return out
+
+
+SHAPES = [(1, 1, 1), (1, 2, 31), (2, 1, 64), (1, 1, 100), (1, 2, 129), (1, 1, 257)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_shapes(B, H, N, d, causal):
+    run_case(B, H, N, d, causal, seed=2000 + B * 100 + H * 10 + N + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_end_to_end(causal):
+    """fa_fwd's own o and lse feed fa_bwd."""
+    run_case(2, 2, 300, 128, causal, seed=2500, forward="gpu")
+    run_case(1, 3, 200, 64, causal, seed=2501, forward="gpu")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.35])
+def test_backward_scales(scale):
+    run_case(1, 2, 96, 64, False, seed=2600, scale=scale)
+    run_case(1, 1, 96, 128, True, seed=2601, scale=scale)
+
+
+def test_backward_medium():
+    """Several key blocks and query blocks, both masks, end to end."""
+    run_case(1, 4, 1024, 128, True, seed=2700, forward="gpu")
+    run_case(1, 2, 1024, 64, False, seed=2701, forward="gpu")
