@@ -106,8 +106,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int QT = BLK * QP;
   constexpr int STAGE = 2 * QT;         // Q tile, dO tile (elements)
   constexpr int CH = BLK * D / 8;       // 16-byte chunks per tile
-  static_assert(CH % NT == 0 || NT % CH == 0, "tile split");
-  constexpr int CPT = (2 * CH + NT - 1) / NT;   // chunks per thread (Q and dO)
+  static_assert(CH % NT == 0, "tile split");
+  constexpr int CPT = 2 * CH / NT;      // chunks per thread: the first half Q, the rest dO
 
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float sstat[2][2][BLK];   // [buf][lse2, delta][row]
@@ -118,6 +118,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int lr = lane & 31, hh = lane >> 5;
   const int N = a.N;
   const float sl2 = a.sl2;
+  // a negative scale negates the keys held in registers (exact in bf16) and dK at the end
   const uint32_t negmask = a.neg ? 0x80008000u : 0u;
 
   // heads vary fastest; under a causal mask the first key blocks see the most queries, so
@@ -144,7 +145,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const uint16_t* vrow = Vh + (size_t)min(key, N - 1) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      kf[kk] = *(const u32x4*)(krow + 16 * kk + 8 * hh) & keep;
+      kf[kk] = (*(const u32x4*)(krow + 16 * kk + 8 * hh) & keep) ^ negmask;
       vf[kk] = *(const u32x4*)(vrow + 16 * kk + 8 * hh) & keep;
     }
   }
@@ -159,44 +160,36 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int nqb = (N + BLK - 1) / BLK;
   const int qb0 = CAUSAL ? k0 / BLK : 0;
 
-  // staging: chunk c < CH is Q, CH <= c < 2CH is dO; row c/(D/8) of the block, 8 features
+  // staging: chunk c < CH is Q, CH <= c < 2CH is dO; row c/(D/8) of the block, 8 features.
+  // Rows past N repeat row N-1: their probabilities are masked to zero, so they add nothing.
+  // The loaded registers are not touched before they are written to LDS, so the loads stay
+  // in flight over the whole block's compute.
   u32x4 sreg[CPT];
   float st_lse = 0.0f, st_del = 0.0f;
   auto gload = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
-      const int c = tid + r * NT;
-      if (c < 2 * CH) {
-        const int cc = c % CH;
-        const int row = qb * BLK + cc / (D / 8);
-        const int col = (cc % (D / 8)) * 8;
-        const uint16_t* src = c < CH ? Qh : dOh;
-        const uint32_t keep = row < N ? 0xffffffffu : 0u;
-        u32x4 x = *(const u32x4*)(src + (size_t)min(row, N - 1) * D + col) & keep;
-        if (c < CH) x ^= (negmask & keep);
-        sreg[r] = x;
-      }
+      const int cc = tid + (r % (CPT / 2)) * NT;
+      const int row = qb * BLK + cc / (D / 8);
+      const int col = (cc % (D / 8)) * 8;
+      const uint16_t* src = r < CPT / 2 ? Qh : dOh;
+      sreg[r] = *(const u32x4*)(src + (size_t)min(row, N - 1) * D + col);
     }
-    if (tid < BLK) {
-      const int row = min(qb * BLK + tid, N - 1);
-      st_lse = lseh[row] * kLog2e;
-      st_del = delh[row];
-    }
+    const int row = min(qb * BLK + (tid & (BLK - 1)), N - 1);
+    st_lse = lseh[row];
+    st_del = delh[row];
   };
   auto swrite = [&](int buf) __attribute__((always_inline)) {
     uint16_t* base = smem + buf * STAGE;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
-      const int c = tid + r * NT;
-      if (c < 2 * CH) {
-        const int cc = c % CH;
-        const int row = cc / (D / 8);
-        const int col = (cc % (D / 8)) * 8;
-        *(u32x4*)(base + (c < CH ? 0 : QT) + row * QP + col) = sreg[r];
-      }
+      const int cc = tid + (r % (CPT / 2)) * NT;
+      const int row = cc / (D / 8);
+      const int col = (cc % (D / 8)) * 8;
+      *(u32x4*)(base + (r < CPT / 2 ? 0 : QT) + row * QP + col) = sreg[r];
     }
     if (tid < BLK) {
-      sstat[buf][0][tid] = st_lse;
+      sstat[buf][0][tid] = st_lse * kLog2e;
       sstat[buf][1][tid] = st_del;
     }
   };
@@ -209,40 +202,61 @@ void bwd_dkdv_kernel(BwdArgs a) {
     swrite(0);
   }
   __syncthreads();
+  // Every wave takes every block from qb0 on: a wave whose keys all lie past N, or whose keys
+  // all follow the block's queries (causal), sees only masked probabilities and adds zeros.
+  // That keeps the loop free of branches around the accumulators.
   for (int qb = qb0; qb < nqb; ++qb) {
     const int buf = (qb - qb0) & 1;
-    if (qb + 1 < nqb) gload(qb + 1);
+    gload(min(qb + 1, nqb - 1));
+    // keep the next block's loads at the top of the iteration, in flight over its compute
+    __builtin_amdgcn_sched_barrier(0);
     const uint16_t* Qs = smem + buf * STAGE;
     const uint16_t* dOs = Qs + QT;
     const int qf0 = qb * BLK;   // first query of the block
-    // skip blocks whose queries all precede this wave's keys (causal), and waves past N
-    if ((!CAUSAL || qf0 + BLK - 1 >= kw0) && kw0 < N) {
-      // S = Q K^T, dP = dO V^T: lane = key, register i = query 8(i/4) + 4hh + i%4
+    {
+      // S = Q K^T, dP = dO V^T: lane = key, register i = query 8(i/4) + 4hh + i%4.
+      // All LDS operands of the block are read up front so that their latency overlaps the
+      // products; the transposed ones for dV and dK do not depend on the softmax.
+      u32x4 qa[D / 16], da[D / 16], tq[D / 32][2], tdo[D / 32][2];
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l4[g] = *(const f32x4*)(&sstat[buf][0][8 * g + 4 * hh]);
+        d4[g] = *(const f32x4*)(&sstat[buf][1][8 * g + 4 * hh]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        qa[kk] = *(const u32x4*)(Qs + lr * QP + 16 * kk + 8 * hh);
+        da[kk] = *(const u32x4*)(dOs + lr * QP + 16 * kk + 8 * hh);
+      }
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const u32x4 qa = *(const u32x4*)(Qs + lr * QP + 16 * kk + 8 * hh);
-        const u32x4 da = *(const u32x4*)(dOs + lr * QP + 16 * kk + 8 * hh);
-        s = mfma(qa, kf[kk], s);
-        dp = mfma(da, vf[kk], dp);
+        s = mfma(qa[kk], kf[kk], s);
+        dp = mfma(da[kk], vf[kk], dp);
       }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          tdo[dt][c] = read_tr<QP>(dOs, c, dt, tr_row, tr_col);
+          tq[dt][c] = read_tr<QP>(Qs, c, dt, tr_row, tr_col);
+        }
       const bool masked = (qf0 + BLK > N) || (kw0 + BLK > N) || (CAUSAL && qf0 < kw0 + BLK - 1);
       u32x4 pb[2], db[2];
       float p[16], ds[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *(const f32x4*)(&sstat[buf][0][8 * g + 4 * hh]);
-        const f32x4 d4 = *(const f32x4*)(&sstat[buf][1][8 * g + 4 * hh]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int i = 4 * g + t;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -l4[t]));
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -l4[g][t]));
           if (masked) {
             const int qi = qf0 + 8 * g + 4 * hh + t;
             if (qi >= N || key >= N || (CAUSAL && key > qi)) pv = 0.0f;
           }
           p[i] = pv;
-          ds[i] = pv * (dp[i] - d4[t]);
+          ds[i] = pv * (dp[i] - d4[g][t]);
         }
       }
 #pragma unroll
@@ -257,17 +271,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          dv[dt] = mfma(read_tr<QP>(dOs, c, dt, tr_row, tr_col), pb[c], dv[dt]);
-          dk[dt] = mfma(read_tr<QP>(Qs, c, dt, tr_row, tr_col), db[c], dk[dt]);
+          dv[dt] = mfma(tdo[dt][c], pb[c], dv[dt]);
+          dk[dt] = mfma(tq[dt][c], db[c], dk[dt]);
         }
     }
-    if (qb + 1 < nqb) swrite(buf ^ 1);
+    swrite(buf ^ 1);
     __syncthreads();
   }
 
-  // dK = |scale| * (Q'^T dS)^T, dV as accumulated; lane = key, registers = features
+  // dK = scale * (Q^T dS)^T, dV as accumulated; lane = key, registers = features
   if (key < N) {
-    const float kscale = sl2 / kLog2e;
+    const float kscale = (a.neg ? -sl2 : sl2) / kLog2e;
     uint16_t* dkrow = (uint16_t*)a.dk + head + (size_t)key * D;
     uint16_t* dvrow = (uint16_t*)a.dv + head + (size_t)key * D;
 #pragma unroll
