@@ -308,7 +308,8 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int KT = BLK * KP, VT = BLK * VP;
   constexpr int STAGE = KT + VT;
   constexpr int CH = BLK * D / 8;
-  constexpr int CPT = (2 * CH + NT - 1) / NT;
+  static_assert(CH % NT == 0, "tile split");
+  constexpr int CPT = 2 * CH / NT;      // chunks per thread: the first half K, the rest V
 
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
@@ -358,33 +359,28 @@ void bwd_dq_kernel(BwdArgs a) {
   const int kv_end = CAUSAL ? min(N, q0 + NW * BLK) : N;
   const int nkt = (kv_end + BLK - 1) / BLK;
 
+  // Key rows past N repeat row N-1; their probabilities are masked to zero. The loaded
+  // registers are not touched before they are written to LDS (loads stay in flight).
   u32x4 sreg[CPT];
   auto gload = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
-      const int c = tid + r * NT;
-      if (c < 2 * CH) {
-        const int cc = c % CH;
-        const int row = t * BLK + cc / (D / 8);
-        const int col = (cc % (D / 8)) * 8;
-        const uint16_t* src = c < CH ? Kh : Vh;
-        const uint32_t kp = row < N ? 0xffffffffu : 0u;
-        sreg[r] = *(const u32x4*)(src + (size_t)min(row, N - 1) * D + col) & kp;
-      }
+      const int cc = tid + (r % (CPT / 2)) * NT;
+      const int row = t * BLK + cc / (D / 8);
+      const int col = (cc % (D / 8)) * 8;
+      const uint16_t* src = r < CPT / 2 ? Kh : Vh;
+      sreg[r] = *(const u32x4*)(src + (size_t)min(row, N - 1) * D + col);
     }
   };
   auto swrite = [&](int buf) __attribute__((always_inline)) {
     uint16_t* base = smem + buf * STAGE;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
-      const int c = tid + r * NT;
-      if (c < 2 * CH) {
-        const int cc = c % CH;
-        const int row = cc / (D / 8);
-        const int col = (cc % (D / 8)) * 8;
-        if (c < CH) *(u32x4*)(base + row * KP + col) = sreg[r];
-        else *(u32x4*)(base + KT + row * VP + col) = sreg[r];
-      }
+      const int cc = tid + (r % (CPT / 2)) * NT;
+      const int row = cc / (D / 8);
+      const int col = (cc % (D / 8)) * 8;
+      if (r < CPT / 2) *(u32x4*)(base + row * KP + col) = sreg[r];
+      else *(u32x4*)(base + KT + row * VP + col) = sreg[r];
     }
   };
 
@@ -394,13 +390,16 @@ void bwd_dq_kernel(BwdArgs a) {
   gload(0);
   swrite(0);
   __syncthreads();
+  // Every wave takes every key tile: tiles past a wave's last query (causal) or waves past N
+  // see only masked probabilities and add zeros, which keeps the loop free of branches.
   for (int t = 0; t < nkt; ++t) {
     const int buf = t & 1;
-    if (t + 1 < nkt) gload(t + 1);
+    gload(min(t + 1, nkt - 1));
+    __builtin_amdgcn_sched_barrier(0);
     const uint16_t* Ks = smem + buf * STAGE;
     const uint16_t* Vs = Ks + KT;
     const int key0 = t * BLK;
-    if ((!CAUSAL || key0 <= qw0 + BLK - 1) && qw0 < N) {
+    {
       // S^T = K Q'^T, dP^T = V dO^T: lane = query, register i = key 8(i/4) + 4hh + i%4
       f32x16 s = {}, dp = {};
 #pragma unroll
@@ -432,7 +431,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) dq[dt] = mfma(read_tr<KP>(Ks, c, dt, tr_row, tr_col), db[c], dq[dt]);
     }
-    if (t + 1 < nkt) swrite(buf ^ 1);
+    swrite(buf ^ 1);
     __syncthreads();
   }
 
