@@ -99,27 +99,37 @@ void bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict
 }
 
 // ---- dK, dV --------------------------------------------------------------------------------
+// A workgroup owns 128 keys and runs 8 waves in two roles, two waves per SIMD:
+// * score waves (0..3) hold K^T and V^T of 32 keys each in registers and, per query block,
+//   form S = Q K^T and dP = dO V^T, the probabilities P and dS = P (dP - delta), and hand
+//   P and dS (bf16, already in B-operand order) to their partner through LDS;
+// * accumulator waves (4..7) hold dK^T and dV^T of the same 32 keys and, one block later,
+//   add dO^T P and Q^T dS with the transposed operands read from the staged tiles.
+// Each role fits in half a SIMD's registers, so a score wave's softmax runs while its
+// partner on the same SIMD keeps the matrix core busy. Q / dO tiles rotate through three
+// LDS buffers (block j+1 loading, j scored, j-1 accumulated); P / dS through two.
+constexpr int DKDV_NT = 2 * NT;          // 8 waves
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NT, 1)
+__global__ __launch_bounds__(DKDV_NT, 1)
 void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int QP = D + 16;            // Q / dO tile pitch (transpose reads conflict-free)
   constexpr int QT = BLK * QP;
   constexpr int STAGE = 2 * QT;         // Q tile, dO tile (elements)
   constexpr int CH = BLK * D / 8;       // 16-byte chunks per tile
-  static_assert(CH % NT == 0, "tile split");
-  constexpr int CPT = 2 * CH / NT;      // chunks per thread: the first half Q, the rest dO
+  static_assert((2 * CH) % DKDV_NT == 0, "tile split");
+  constexpr int CPT = 2 * CH / DKDV_NT; // chunks per thread
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
-  __shared__ __attribute__((aligned(16))) float sstat[2][2][BLK];   // [buf][lse2, delta][row]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * STAGE];
+  __shared__ __attribute__((aligned(16))) float sstat[3][2][BLK];       // [buf][lse2, delta][row]
+  __shared__ __attribute__((aligned(16))) u32x4 xch[2][NW][4][64];      // [buf][pair][pb0 pb1 db0 db1][lane]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & (NW - 1);
   const int lr = lane & 31, hh = lane >> 5;
   const int N = a.N;
   const float sl2 = a.sl2;
-  // a negative scale negates the keys held in registers (exact in bf16) and dK at the end
-  const uint32_t negmask = a.neg ? 0x80008000u : 0u;
 
   // heads vary fastest; under a causal mask the first key blocks see the most queries, so
   // the dispatch order is already heaviest first
@@ -127,52 +137,32 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int kblk = id / a.BH;
   const int bh = id - kblk * a.BH;
   const int k0 = kblk * NW * BLK;
-  const int kw0 = k0 + wave * BLK;      // this wave's first key
+  const int kw0 = k0 + pair * BLK;      // the pair's first key
+  const int key = kw0 + lr;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ Qh = (const uint16_t*)a.q + head;
-  const uint16_t* __restrict__ Kh = (const uint16_t*)a.k + head;
-  const uint16_t* __restrict__ Vh = (const uint16_t*)a.v + head;
   const uint16_t* __restrict__ dOh = (const uint16_t*)a.dout + head;
   const float* __restrict__ lseh = a.lse + (size_t)bh * N;
   const float* __restrict__ delh = a.delta + (size_t)bh * N;
 
-  // K^T and V^T as B operands: lane l supplies key kw0 + l%32, features 16kk + 8hh .. +7
-  const int key = kw0 + lr;
-  u32x4 kf[D / 16], vf[D / 16];
-  {
-    const uint32_t keep = key < N ? 0xffffffffu : 0u;
-    const uint16_t* krow = Kh + (size_t)min(key, N - 1) * D;
-    const uint16_t* vrow = Vh + (size_t)min(key, N - 1) * D;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kf[kk] = (*(const u32x4*)(krow + 16 * kk + 8 * hh) & keep) ^ negmask;
-      vf[kk] = *(const u32x4*)(vrow + 16 * kk + 8 * hh) & keep;
-    }
-  }
-
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
-
-  // query blocks: causal ones start at the first block that holds a query >= k0
+  // query blocks: causal ones start at the first block that holds a query >= k0. Every pair
+  // takes every block from there: a pair whose keys lie past N, or follow all of a block's
+  // queries, sees only masked probabilities and adds zeros (no branches around accumulators).
   const int nqb = (N + BLK - 1) / BLK;
   const int qb0 = CAUSAL ? k0 / BLK : 0;
 
-  // staging: chunk c < CH is Q, CH <= c < 2CH is dO; row c/(D/8) of the block, 8 features.
-  // Rows past N repeat row N-1: their probabilities are masked to zero, so they add nothing.
-  // The loaded registers are not touched before they are written to LDS, so the loads stay
-  // in flight over the whole block's compute.
+  // staging of block qb by all 8 waves: chunk c < CH is Q, CH <= c < 2CH is dO; rows past N
+  // repeat row N-1 (masked). The loaded registers are untouched until written to LDS.
   u32x4 sreg[CPT];
   float st_lse = 0.0f, st_del = 0.0f;
   auto gload = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
-      const int cc = tid + (r % (CPT / 2)) * NT;
+      const int c = tid + r * DKDV_NT;
+      const int cc = c < CH ? c : c - CH;
       const int row = qb * BLK + cc / (D / 8);
       const int col = (cc % (D / 8)) * 8;
-      const uint16_t* src = r < CPT / 2 ? Qh : dOh;
+      const uint16_t* src = c < CH ? Qh : dOh;
       sreg[r] = *(const u32x4*)(src + (size_t)min(row, N - 1) * D + col);
     }
     const int row = min(qb * BLK + (tid & (BLK - 1)), N - 1);
@@ -183,10 +173,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
     uint16_t* base = smem + buf * STAGE;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
-      const int cc = tid + (r % (CPT / 2)) * NT;
+      const int c = tid + r * DKDV_NT;
+      const int cc = c < CH ? c : c - CH;
       const int row = cc / (D / 8);
       const int col = (cc % (D / 8)) * 8;
-      *(u32x4*)(base + (r < CPT / 2 ? 0 : QT) + row * QP + col) = sreg[r];
+      *(u32x4*)(base + (c < CH ? 0 : QT) + row * QP + col) = sreg[r];
     }
     if (tid < BLK) {
       sstat[buf][0][tid] = st_lse * kLog2e;
@@ -194,63 +185,58 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  const int tr_row = 4 * hh + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  if (qb0 < nqb) {
-    gload(qb0);
-    swrite(0);
-  }
+  gload(qb0);
+  swrite(0);
   __syncthreads();
-  // Every wave takes every block from qb0 on: a wave whose keys all lie past N, or whose keys
-  // all follow the block's queries (causal), sees only masked probabilities and adds zeros.
-  // That keeps the loop free of branches around the accumulators.
-  for (int qb = qb0; qb < nqb; ++qb) {
-    const int buf = (qb - qb0) & 1;
-    gload(min(qb + 1, nqb - 1));
-    // keep the next block's loads at the top of the iteration, in flight over its compute
-    __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* Qs = smem + buf * STAGE;
-    const uint16_t* dOs = Qs + QT;
-    const int qf0 = qb * BLK;   // first query of the block
+
+  if (wave < NW) {
+    // ---- score role ----
+    // K^T and V^T as B operands: lane l supplies key kw0 + l%32, features 16kk + 8hh .. +7;
+    // a negative scale negates the keys (exact in bf16), and dK's sign comes at the end
+    const uint32_t negmask = a.neg ? 0x80008000u : 0u;
+    const uint16_t* __restrict__ Kh = (const uint16_t*)a.k + head;
+    const uint16_t* __restrict__ Vh = (const uint16_t*)a.v + head;
+    u32x4 kf[D / 16], vf[D / 16];
     {
-      // S = Q K^T, dP = dO V^T: lane = key, register i = query 8(i/4) + 4hh + i%4.
-      // All LDS operands of the block are read up front so that their latency overlaps the
-      // products; the transposed ones for dV and dK do not depend on the softmax.
-      u32x4 qa[D / 16], da[D / 16], tq[D / 32][2], tdo[D / 32][2];
+      const uint32_t keep = key < N ? 0xffffffffu : 0u;
+      const uint16_t* krow = Kh + (size_t)min(key, N - 1) * D;
+      const uint16_t* vrow = Vh + (size_t)min(key, N - 1) * D;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        kf[kk] = (*(const u32x4*)(krow + 16 * kk + 8 * hh) & keep) ^ negmask;
+        vf[kk] = *(const u32x4*)(vrow + 16 * kk + 8 * hh) & keep;
+      }
+    }
+    int cur = 0;   // LDS buffer of block qb
+    for (int qb = qb0; qb < nqb; ++qb) {
+      gload(min(qb + 1, nqb - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* Qs = smem + cur * STAGE;
+      const uint16_t* dOs = Qs + QT;
+      const int qf0 = qb * BLK;
       f32x4 l4[4], d4[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        l4[g] = *(const f32x4*)(&sstat[buf][0][8 * g + 4 * hh]);
-        d4[g] = *(const f32x4*)(&sstat[buf][1][8 * g + 4 * hh]);
+        l4[g] = *(const f32x4*)(&sstat[cur][0][8 * g + 4 * hh]);
+        d4[g] = *(const f32x4*)(&sstat[cur][1][8 * g + 4 * hh]);
       }
+      // S = Q K^T, dP = dO V^T: lane = key, register i = query 8(i/4) + 4hh + i%4
+      f32x16 sc = {}, dp = {};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        qa[kk] = *(const u32x4*)(Qs + lr * QP + 16 * kk + 8 * hh);
-        da[kk] = *(const u32x4*)(dOs + lr * QP + 16 * kk + 8 * hh);
+        const u32x4 qa = *(const u32x4*)(Qs + lr * QP + 16 * kk + 8 * hh);
+        const u32x4 da = *(const u32x4*)(dOs + lr * QP + 16 * kk + 8 * hh);
+        sc = mfma(qa, kf[kk], sc);
+        dp = mfma(da, vf[kk], dp);
       }
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma(qa[kk], kf[kk], s);
-        dp = mfma(da[kk], vf[kk], dp);
-      }
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          tdo[dt][c] = read_tr<QP>(dOs, c, dt, tr_row, tr_col);
-          tq[dt][c] = read_tr<QP>(Qs, c, dt, tr_row, tr_col);
-        }
       const bool masked = (qf0 + BLK > N) || (kw0 + BLK > N) || (CAUSAL && qf0 < kw0 + BLK - 1);
-      u32x4 pb[2], db[2];
       float p[16], ds[16];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int i = 4 * g + t;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -l4[g][t]));
+          float pv = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -l4[g][t]));
           if (masked) {
             const int qi = qf0 + 8 * g + 4 * hh + t;
             if (qi >= N || key >= N || (CAUSAL && key > qi)) pv = 0.0f;
@@ -258,14 +244,51 @@ void bwd_dkdv_kernel(BwdArgs a) {
           p[i] = pv;
           ds[i] = pv * (dp[i] - d4[g][t]);
         }
-      }
+      u32x4* xo = &xch[(qb - qb0) & 1][pair][0][lane];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        pb[c] = (u32x4){pack_bf16x2(p[8 * c + 0], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
-                        pack_bf16x2(p[8 * c + 4], p[8 * c + 5]), pack_bf16x2(p[8 * c + 6], p[8 * c + 7])};
-        db[c] = (u32x4){pack_bf16x2(ds[8 * c + 0], ds[8 * c + 1]), pack_bf16x2(ds[8 * c + 2], ds[8 * c + 3]),
-                        pack_bf16x2(ds[8 * c + 4], ds[8 * c + 5]), pack_bf16x2(ds[8 * c + 6], ds[8 * c + 7])};
+        xo[64 * c] = (u32x4){pack_bf16x2(p[8 * c + 0], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
+                             pack_bf16x2(p[8 * c + 4], p[8 * c + 5]), pack_bf16x2(p[8 * c + 6], p[8 * c + 7])};
+        xo[64 * (2 + c)] = (u32x4){pack_bf16x2(ds[8 * c + 0], ds[8 * c + 1]), pack_bf16x2(ds[8 * c + 2], ds[8 * c + 3]),
+                                   pack_bf16x2(ds[8 * c + 4], ds[8 * c + 5]), pack_bf16x2(ds[8 * c + 6], ds[8 * c + 7])};
       }
+      // block qb + 1 goes to the next buffer, where the next iteration finds it
+      cur = cur == 2 ? 0 : cur + 1;
+      swrite(cur);
+      __syncthreads();
+    }
+    __syncthreads();   // the accumulators' last block
+  } else {
+    // ---- accumulator role ----
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    // first step: the score waves take block qb0, nothing to accumulate yet
+    gload(min(qb0 + 1, nqb - 1));
+    swrite(1);
+    __syncthreads();
+    int prev = 0;  // LDS buffer of block qb - 1
+    for (int qb = qb0 + 1; qb <= nqb; ++qb) {
+      gload(min(qb + 1, nqb - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* Qs = smem + prev * STAGE;
+      const uint16_t* dOs = Qs + QT;
+      const u32x4* xi = &xch[(qb - 1 - qb0) & 1][pair][0][lane];
+      u32x4 tq[D / 32][2], tdo[D / 32][2];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          tdo[dt][c] = read_tr<QP>(dOs, c, dt, tr_row, tr_col);
+          tq[dt][c] = read_tr<QP>(Qs, c, dt, tr_row, tr_col);
+        }
+      const u32x4 pb[2] = {xi[0], xi[64]};
+      const u32x4 db[2] = {xi[128], xi[192]};
       // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query chunks
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
@@ -274,28 +297,30 @@ void bwd_dkdv_kernel(BwdArgs a) {
           dv[dt] = mfma(tdo[dt][c], pb[c], dv[dt]);
           dk[dt] = mfma(tq[dt][c], db[c], dk[dt]);
         }
+      // buffers: block qb - 1 was in prev, block qb + 1 goes to prev + 2 (mod 3)
+      swrite(prev == 0 ? 2 : prev - 1);
+      prev = prev == 2 ? 0 : prev + 1;
+      __syncthreads();
     }
-    swrite(buf ^ 1);
-    __syncthreads();
-  }
 
-  // dK = scale * (Q^T dS)^T, dV as accumulated; lane = key, registers = features
-  if (key < N) {
-    const float kscale = (a.neg ? -sl2 : sl2) / kLog2e;
-    uint16_t* dkrow = (uint16_t*)a.dk + head + (size_t)key * D;
-    uint16_t* dvrow = (uint16_t*)a.dv + head + (size_t)key * D;
+    // dK = scale * (Q^T dS)^T, dV as accumulated; lane = key, registers = features
+    if (key < N) {
+      const float kscale = (a.neg ? -sl2 : sl2) / kLog2e;
+      uint16_t* dkrow = (uint16_t*)a.dk + head + (size_t)key * D;
+      uint16_t* dvrow = (uint16_t*)a.dv + head + (size_t)key * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = dt * 32 + 8 * g + 4 * hh;
-        const u32x2 wk = {pack_bf16x2(dk[dt][4 * g + 0] * kscale, dk[dt][4 * g + 1] * kscale),
-                          pack_bf16x2(dk[dt][4 * g + 2] * kscale, dk[dt][4 * g + 3] * kscale)};
-        const u32x2 wv = {pack_bf16x2(dv[dt][4 * g + 0], dv[dt][4 * g + 1]),
-                          pack_bf16x2(dv[dt][4 * g + 2], dv[dt][4 * g + 3])};
-        *(u32x2*)(dkrow + col) = wk;
-        *(u32x2*)(dvrow + col) = wv;
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int col = dt * 32 + 8 * g + 4 * hh;
+          const u32x2 wk = {pack_bf16x2(dk[dt][4 * g + 0] * kscale, dk[dt][4 * g + 1] * kscale),
+                            pack_bf16x2(dk[dt][4 * g + 2] * kscale, dk[dt][4 * g + 3] * kscale)};
+          const u32x2 wv = {pack_bf16x2(dv[dt][4 * g + 0], dv[dt][4 * g + 1]),
+                            pack_bf16x2(dv[dt][4 * g + 2], dv[dt][4 * g + 3])};
+          *(u32x2*)(dkrow + col) = wk;
+          *(u32x2*)(dvrow + col) = wv;
+        }
+    }
   }
 }
 
@@ -457,7 +482,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
                      (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
   const unsigned nblk = (unsigned)((a.N + NW * BLK - 1) / (NW * BLK));
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(DKDV_NT), 0, stream, a);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
