@@ -64,14 +64,46 @@ __device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32
                                                  0, 0, 0);
 }
 
-// Transposed operand from a row-major [row][feature] LDS tile (pitch P elements): lane l gets
-// feature 32*dt + l%32 for rows 16*c16 + {4hh + r, 8 + 4hh + r} (r = 0..3), the order in
-// which the accumulator registers 8c..8c+7 hold their rows.
-template <int P>
-__device__ __forceinline__ u32x4 read_tr(const uint16_t* tile, int c16, int dt, int tr_row, int tr_col) {
-  const uint16_t* base = tile + (c16 * 16 + tr_row) * P + dt * 32 + tr_col;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * P));
+// Staged [32][D] bf16 tiles sit in LDS without padding: 16-byte chunk L of row r is stored at
+// chunk position L ^ swz(r). With this permutation the 16 rows that one 16-lane quarter of a
+// 16-byte row read touches land in 16 different bank groups, and the 4 rows x 4 chunks that
+// each half of a transposed read touches do too, so neither access pattern conflicts.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "head width");
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int chunk) { return r * D + 8 * (chunk ^ swz<D>(r)); }
+
+// Per-lane element offsets into a swizzled tile for the two read patterns:
+// * row reads: lane l takes row l%32, features 16kk + 8(l/32) .. +7 (an A operand of S);
+// * transposed reads: lane l gets feature 32dt + l%32 of rows 16c + {4hh + r, 8 + 4hh + r}
+//   (r = 0..3), the order in which accumulator registers 8c..8c+7 hold their rows; the
+//   offsets below are for c = 0, and c = 1 adds 16 rows.
+template <int D>
+struct TileOffsets {
+  int row[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ explicit TileOffsets(int lane) {
+    const int lr = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) row[kk] = tile_off<D>(lr, 2 * kk + hh);
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        tr[dt][h] = tile_off<D>(tr_row + 8 * h, 4 * dt + (tr_col >> 3)) + (tr_col & 7);
+  }
+};
+
+template <int D>
+__device__ __forceinline__ u32x4 read_tr(const uint16_t* tile, int c16, const TileOffsets<D>& to, int dt) {
+  const uint16_t* base = tile + c16 * 16 * D;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + to.tr[dt][0]));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + to.tr[dt][1]));
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
   return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
 }
@@ -112,9 +144,8 @@ constexpr int DKDV_NT = 2 * NT;          // 8 waves
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DKDV_NT, 1)
 void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int QP = D + 16;            // Q / dO tile pitch (transpose reads conflict-free)
-  constexpr int QT = BLK * QP;
-  constexpr int STAGE = 2 * QT;         // Q tile, dO tile (elements)
+  constexpr int QT = BLK * D;           // swizzled Q / dO tile (elements)
+  constexpr int STAGE = 2 * QT;         // Q tile, dO tile
   constexpr int CH = BLK * D / 8;       // 16-byte chunks per tile
   static_assert((2 * CH) % DKDV_NT == 0, "tile split");
   constexpr int CPT = 2 * CH / DKDV_NT; // chunks per thread
@@ -175,9 +206,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + r * DKDV_NT;
       const int cc = c < CH ? c : c - CH;
-      const int row = cc / (D / 8);
-      const int col = (cc % (D / 8)) * 8;
-      *(u32x4*)(base + (c < CH ? 0 : QT) + row * QP + col) = sreg[r];
+      *(u32x4*)(base + (c < CH ? 0 : QT) + tile_off<D>(cc / (D / 8), cc % (D / 8))) = sreg[r];
     }
     if (tid < BLK) {
       sstat[buf][0][tid] = st_lse * kLog2e;
@@ -185,6 +214,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
+  const TileOffsets<D> to(lane);
   gload(qb0);
   swrite(0);
   __syncthreads();
@@ -224,8 +254,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
       f32x16 sc = {}, dp = {};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const u32x4 qa = *(const u32x4*)(Qs + lr * QP + 16 * kk + 8 * hh);
-        const u32x4 da = *(const u32x4*)(dOs + lr * QP + 16 * kk + 8 * hh);
+        const u32x4 qa = *(const u32x4*)(Qs + to.row[kk]);
+        const u32x4 da = *(const u32x4*)(dOs + to.row[kk]);
         sc = mfma(qa, kf[kk], sc);
         dp = mfma(da, vf[kk], dp);
       }
@@ -265,9 +295,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
-    const int tr_row = 4 * hh + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
     // first step: the score waves take block qb0, nothing to accumulate yet
     gload(min(qb0 + 1, nqb - 1));
     swrite(1);
@@ -284,8 +311,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          tdo[dt][c] = read_tr<QP>(dOs, c, dt, tr_row, tr_col);
-          tq[dt][c] = read_tr<QP>(Qs, c, dt, tr_row, tr_col);
+          tdo[dt][c] = read_tr<D>(dOs, c, to, dt);
+          tq[dt][c] = read_tr<D>(Qs, c, to, dt);
         }
       const u32x4 pb[2] = {xi[0], xi[64]};
       const u32x4 db[2] = {xi[128], xi[192]};
@@ -328,10 +355,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2)
 void bwd_dq_kernel(BwdArgs a) {
-  constexpr int KP = D + 16;            // K tile pitch (row reads and transpose reads)
-  constexpr int VP = D + 8;             // V tile pitch (row reads)
-  constexpr int KT = BLK * KP, VT = BLK * VP;
-  constexpr int STAGE = KT + VT;
+  constexpr int KT = BLK * D;           // swizzled K / V tiles (elements)
+  constexpr int STAGE = 2 * KT;
   constexpr int CH = BLK * D / 8;
   static_assert(CH % NT == 0, "tile split");
   constexpr int CPT = 2 * CH / NT;      // chunks per thread: the first half K, the rest V
@@ -402,16 +427,11 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int cc = tid + (r % (CPT / 2)) * NT;
-      const int row = cc / (D / 8);
-      const int col = (cc % (D / 8)) * 8;
-      if (r < CPT / 2) *(u32x4*)(base + row * KP + col) = sreg[r];
-      else *(u32x4*)(base + KT + row * VP + col) = sreg[r];
+      *(u32x4*)(base + (r < CPT / 2 ? 0 : KT) + tile_off<D>(cc / (D / 8), cc % (D / 8))) = sreg[r];
     }
   };
 
-  const int tr_row = 4 * hh + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
+  const TileOffsets<D> to(lane);
   gload(0);
   swrite(0);
   __syncthreads();
@@ -429,8 +449,8 @@ void bwd_dq_kernel(BwdArgs a) {
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const u32x4 ka = *(const u32x4*)(Ks + lr * KP + 16 * kk + 8 * hh);
-        const u32x4 va = *(const u32x4*)(Vs + lr * VP + 16 * kk + 8 * hh);
+        const u32x4 ka = *(const u32x4*)(Ks + to.row[kk]);
+        const u32x4 va = *(const u32x4*)(Vs + to.row[kk]);
         s = mfma(ka, qf[kk], s);
         dp = mfma(va, df[kk], dp);
       }
@@ -454,7 +474,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) dq[dt] = mfma(read_tr<KP>(Ks, c, dt, tr_row, tr_col), db[c], dq[dt]);
+        for (int c = 0; c < 2; ++c) dq[dt] = mfma(read_tr<D>(Ks, c, to, dt), db[c], dq[dt]);
     }
     swrite(buf ^ 1);
     __syncthreads();
