@@ -131,6 +131,34 @@ void bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict
 }
 
 // ---- dK, dV --------------------------------------------------------------------------------
+// One 16-byte-per-lane (or 4-byte-per-lane) global -> LDS load: lane l's data lands at LDS
+// byte lds_addr + 16 l (+ 4 l). Issued through inline assembly so that the compiler's wait
+// insertion does not tie later LDS reads to it; completion is tracked by hand (step_barrier).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding and its LDS
+// accesses have completed, then join the workgroup barrier. The compiler does not see the
+// LDS writes of the loads above, so this is also a compiler memory barrier.
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  constexpr int imm = (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+template <int n>
+__device__ __forceinline__ void step_barrier() {
+  wait_vm_lgkm0<n>();
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // A workgroup owns 128 keys and runs 8 waves in two roles, two waves per SIMD:
 // * score waves (0..3) hold K^T and V^T of 32 keys each in registers and, per query block,
 //   form S = Q K^T and dP = dO V^T, the probabilities P and dS = P (dP - delta), and hand
@@ -138,20 +166,26 @@ void bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict
 // * accumulator waves (4..7) hold dK^T and dV^T of the same 32 keys and, one block later,
 //   add dO^T P and Q^T dS with the transposed operands read from the staged tiles.
 // Each role fits in half a SIMD's registers, so a score wave's softmax runs while its
-// partner on the same SIMD keeps the matrix core busy. Q / dO tiles rotate through three
-// LDS buffers (block j+1 loading, j scored, j-1 accumulated); P / dS through two.
+// partner on the same SIMD keeps the matrix core busy. The query blocks (Q and dO tiles,
+// log-normaliser and delta rows) rotate through four LDS slots, loaded straight from global
+// memory two blocks ahead: block j+2 loading, j+1 landed, j scored, j-1 accumulated.
+// P / dS rotate through two exchange buffers.
 constexpr int DKDV_NT = 2 * NT;          // 8 waves
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DKDV_NT, 1)
 void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int QT = BLK * D;           // swizzled Q / dO tile (elements)
-  constexpr int STAGE = 2 * QT;         // Q tile, dO tile
-  constexpr int CH = BLK * D / 8;       // 16-byte chunks per tile
-  static_assert((2 * CH) % DKDV_NT == 0, "tile split");
-  constexpr int CPT = 2 * CH / DKDV_NT; // chunks per thread
+  constexpr int TILEB = 2 * QT;         // bytes per tile
+  constexpr int SLOTB = 2 * TILEB + 512;   // Q tile, dO tile, 64 floats of log-normaliser, 64 of delta
+  constexpr int SLOTS = 4;
+  constexpr int NC = D / 8;             // 16-byte chunks per row
+  constexpr int IPW = D / 64;           // 1 KiB loads per wave per block (Q and dO: 2 TILEB)
+  constexpr int KB_TILE = TILEB / 1024; // 1 KiB regions per tile
+  static_assert(2 * KB_TILE == 8 * IPW, "8 waves load the two tiles");
+  // vector-memory operations per block: the tiles, plus the row statistics on waves 0 and 1
+  constexpr int OPS_STAT = IPW + 1, OPS_TILE = IPW;
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * STAGE];
-  __shared__ __attribute__((aligned(16))) float sstat[3][2][BLK];       // [buf][lse2, delta][row]
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SLOTS * SLOTB];
   __shared__ __attribute__((aligned(16))) u32x4 xch[2][NW][4][64];      // [buf][pair][pb0 pb1 db0 db1][lane]
 
   const int tid = threadIdx.x;
@@ -171,53 +205,59 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int kw0 = k0 + pair * BLK;      // the pair's first key
   const int key = kw0 + lr;
   const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Qh = (const uint16_t*)a.q + head;
-  const uint16_t* __restrict__ dOh = (const uint16_t*)a.dout + head;
-  const float* __restrict__ lseh = a.lse + (size_t)bh * N;
-  const float* __restrict__ delh = a.delta + (size_t)bh * N;
 
   // query blocks: causal ones start at the first block that holds a query >= k0. Every pair
   // takes every block from there: a pair whose keys lie past N, or follow all of a block's
   // queries, sees only masked probabilities and adds zeros (no branches around accumulators).
   const int nqb = (N + BLK - 1) / BLK;
   const int qb0 = CAUSAL ? k0 / BLK : 0;
+  const int nq = nqb - qb0;
 
-  // staging of block qb by all 8 waves: chunk c < CH is Q, CH <= c < 2CH is dO; rows past N
-  // repeat row N-1 (masked). The loaded registers are untouched until written to LDS.
-  u32x4 sreg[CPT];
-  float st_lse = 0.0f, st_del = 0.0f;
-  auto gload = [&](int qb) __attribute__((always_inline)) {
+  // ---- loads of one block into a slot -------------------------------------------------------
+  // Wave w fills 1 KiB regions w*IPW .. w*IPW+IPW-1 of the slot's two tiles: lane l writes
+  // physical chunk l % NC of row kb*(512/D) + l / NC, so it loads that row's logical chunk
+  // (physical ^ swz(row)). Rows past N repeat row N-1 (masked later). Waves 0 and 1 also load
+  // the block's 32 log-normalisers and deltas (lanes 32..63 repeat lanes 0..31).
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
+  const int tile_of_wave = (wave * IPW) / KB_TILE;       // 0: Q, 1: dO
+  const uint8_t* tile_src = (const uint8_t*)(tile_of_wave == 0 ? a.q : a.dout) + head * 2;
+  int dma_row[IPW];
+  uint32_t dma_off[IPW];
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int c = tid + r * DKDV_NT;
-      const int cc = c < CH ? c : c - CH;
-      const int row = qb * BLK + cc / (D / 8);
-      const int col = (cc % (D / 8)) * 8;
-      const uint16_t* src = c < CH ? Qh : dOh;
-      sreg[r] = *(const u32x4*)(src + (size_t)min(row, N - 1) * D + col);
+  for (int i = 0; i < IPW; ++i) {
+    const int kb = (wave * IPW + i) % KB_TILE;
+    const int r = kb * (512 / D) + lane / NC;
+    dma_row[i] = r;
+    dma_off[i] = (uint32_t)(r * 2 * D + 16 * ((lane % NC) ^ swz<D>(r)));
+  }
+  const float* stat_src = wave == 0 ? a.lse + (size_t)bh * N : a.delta + (size_t)bh * N;
+  auto issue = [&](int qb, int slot) __attribute__((always_inline)) {
+    const int row0 = qb * BLK;
+    const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(lds_base + (uint32_t)(slot * SLOTB + tile_of_wave * TILEB)));
+    const uint8_t* src = tile_src + (size_t)row0 * 2 * D;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int over = row0 + dma_row[i] - (N - 1);
+      const uint32_t back = over > 0 ? (uint32_t)over * 2u * D : 0u;
+      const int kb = (wave * IPW + i) % KB_TILE;
+      dma16(src, dma_off[i] - back, dst + (uint32_t)(kb * 1024));
     }
-    const int row = min(qb * BLK + (tid & (BLK - 1)), N - 1);
-    st_lse = lseh[row];
-    st_del = delh[row];
+    if (wave < 2) {
+      const uint32_t sdst = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)(lds_base + (uint32_t)(slot * SLOTB + 2 * TILEB + wave * 256)));
+      dma4(stat_src + row0, (uint32_t)(4 * min(lr, N - 1 - row0)), sdst);
+    }
   };
-  auto swrite = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* base = smem + buf * STAGE;
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int c = tid + r * DKDV_NT;
-      const int cc = c < CH ? c : c - CH;
-      *(u32x4*)(base + (c < CH ? 0 : QT) + tile_off<D>(cc / (D / 8), cc % (D / 8))) = sreg[r];
-    }
-    if (tid < BLK) {
-      sstat[buf][0][tid] = st_lse * kLog2e;
-      sstat[buf][1][tid] = st_del;
-    }
+  auto barrier = [&]() __attribute__((always_inline)) {
+    if (wave < 2) step_barrier<OPS_STAT>();
+    else step_barrier<OPS_TILE>();
   };
 
   const TileOffsets<D> to(lane);
-  gload(qb0);
-  swrite(0);
-  __syncthreads();
+  // blocks qb0 and qb0+1 (a repeat of the last block when there is none) into slots 0 and 1
+  issue(qb0, 0);
+  issue(min(qb0 + 1, nqb - 1), 1);
 
   if (wave < NW) {
     // ---- score role ----
@@ -237,18 +277,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
         vf[kk] = *(const u32x4*)(vrow + 16 * kk + 8 * hh) & keep;
       }
     }
-    int cur = 0;   // LDS buffer of block qb
-    for (int qb = qb0; qb < nqb; ++qb) {
-      gload(min(qb + 1, nqb - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      const uint16_t* Qs = smem + cur * STAGE;
+    // the key operands are plain loads: wait for them before counting the block loads
+    __builtin_amdgcn_s_waitcnt(0xc07f & ~0xc00f);   // vmcnt(0)
+    barrier();   // block qb0 landed (qb0 + 1 may still be in flight)
+    for (int it = 0; it < nq; ++it) {
+      const int qb = qb0 + it;
+      issue(min(qb + 2, nqb - 1), (it + 2) & 3);
+      const uint16_t* Qs = (const uint16_t*)(smem + (it & 3) * SLOTB);
       const uint16_t* dOs = Qs + QT;
+      const float* st = (const float*)(smem + (it & 3) * SLOTB + 2 * TILEB);
       const int qf0 = qb * BLK;
       f32x4 l4[4], d4[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        l4[g] = *(const f32x4*)(&sstat[cur][0][8 * g + 4 * hh]);
-        d4[g] = *(const f32x4*)(&sstat[cur][1][8 * g + 4 * hh]);
+        l4[g] = *(const f32x4*)(st + 8 * g + 4 * hh);
+        d4[g] = *(const f32x4*)(st + 64 + 8 * g + 4 * hh);
       }
       // S = Q K^T, dP = dO V^T: lane = key, register i = query 8(i/4) + 4hh + i%4
       f32x16 sc = {}, dp = {};
@@ -266,7 +309,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int i = 4 * g + t;
-          float pv = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -l4[g][t]));
+          float pv = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -l4[g][t] * kLog2e));
           if (masked) {
             const int qi = qf0 + 8 * g + 4 * hh + t;
             if (qi >= N || key >= N || (CAUSAL && key > qi)) pv = 0.0f;
@@ -274,7 +317,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
           p[i] = pv;
           ds[i] = pv * (dp[i] - d4[g][t]);
         }
-      u32x4* xo = &xch[(qb - qb0) & 1][pair][0][lane];
+      u32x4* xo = &xch[it & 1][pair][0][lane];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         xo[64 * c] = (u32x4){pack_bf16x2(p[8 * c + 0], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
@@ -282,12 +325,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
         xo[64 * (2 + c)] = (u32x4){pack_bf16x2(ds[8 * c + 0], ds[8 * c + 1]), pack_bf16x2(ds[8 * c + 2], ds[8 * c + 3]),
                                    pack_bf16x2(ds[8 * c + 4], ds[8 * c + 5]), pack_bf16x2(ds[8 * c + 6], ds[8 * c + 7])};
       }
-      // block qb + 1 goes to the next buffer, where the next iteration finds it
-      cur = cur == 2 ? 0 : cur + 1;
-      swrite(cur);
-      __syncthreads();
+      barrier();   // block qb + 1 landed; P / dS of block qb visible
     }
-    __syncthreads();   // the accumulators' last block
+    barrier();     // the accumulators' last block
   } else {
     // ---- accumulator role ----
     f32x16 dk[D / 32], dv[D / 32];
@@ -295,17 +335,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
+
+    barrier();   // block qb0 landed
     // first step: the score waves take block qb0, nothing to accumulate yet
-    gload(min(qb0 + 1, nqb - 1));
-    swrite(1);
-    __syncthreads();
-    int prev = 0;  // LDS buffer of block qb - 1
-    for (int qb = qb0 + 1; qb <= nqb; ++qb) {
-      gload(min(qb + 1, nqb - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      const uint16_t* Qs = smem + prev * STAGE;
+    issue(min(qb0 + 2, nqb - 1), 2);
+    barrier();
+    for (int it = 1; it <= nq; ++it) {
+      issue(min(qb0 + it + 2, nqb - 1), (it + 2) & 3);
+      const uint16_t* Qs = (const uint16_t*)(smem + ((it - 1) & 3) * SLOTB);
       const uint16_t* dOs = Qs + QT;
-      const u32x4* xi = &xch[(qb - 1 - qb0) & 1][pair][0][lane];
+      const u32x4* xi = &xch[(it - 1) & 1][pair][0][lane];
       u32x4 tq[D / 32][2], tdo[D / 32][2];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
@@ -324,10 +363,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
           dv[dt] = mfma(tdo[dt][c], pb[c], dv[dt]);
           dk[dt] = mfma(tq[dt][c], db[c], dk[dt]);
         }
-      // buffers: block qb - 1 was in prev, block qb + 1 goes to prev + 2 (mod 3)
-      swrite(prev == 0 ? 2 : prev - 1);
-      prev = prev == 2 ? 0 : prev + 1;
-      __syncthreads();
+      barrier();
     }
 
     // dK = scale * (Q^T dS)^T, dV as accumulated; lane = key, registers = features
@@ -349,6 +385,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
     }
   }
+  // loads of blocks that nothing reads may still be landing: let them finish first
+  wait_vm_lgkm0<0>();
 }
 
 // ---- dQ ------------------------------------------------------------------------------------
