@@ -10,19 +10,18 @@
 //   dS_ij   = P_ij (dP_ij - delta_i)
 //   dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K
 //
-// Three kernels, no atomics:
-// * bwd_delta_kernel: delta per row (fp32), into the caller's workspace.
-// * bwd_dkdv_kernel: a workgroup owns 128 keys (4 waves x 32); it walks the query blocks of
-//   32 rows, staged through LDS (Q, dO, log-normaliser, delta). Per block and wave:
-//     S = Q K^T and dP = dO V^T with K and V held in registers as B operands, so that the
-//     accumulator holds one key per lane and 16 queries in its registers;
-//     dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by
-//     ds_read_b64_tr_b16 from the row-major Q and dO tiles, and P / dS taken from the
-//     accumulator registers as the B operands (the same register/key correspondence as the
-//     forward kernels, with the roles of queries and keys exchanged).
-// * bwd_dq_kernel: a workgroup owns 128 queries (4 waves x 32) and walks the key tiles of
-//   32, like the forward: S^T = K Q^T and dP^T = V dO^T with Q and dO in registers, then
-//   dQ^T += K^T dS^T with K^T read transposed from the K tile.
+// Two kernels, no atomics, launched in this order:
+// * bwd_dq_kernel: a workgroup owns 128 queries (4 waves x 32). Each query's delta comes from
+//   its dO row (held in registers) and its O row, and is written to the caller's workspace.
+//   Then it walks the key tiles of 32, like the forward: S^T = K Q^T and dP^T = V dO^T with
+//   Q and dO in registers, and dQ^T += K^T dS^T with K^T read transposed from the K tile.
+// * bwd_dkdv_kernel: a workgroup owns 128 keys and walks the query blocks of 32 rows, staged
+//   in LDS (Q, dO, log-normaliser, delta). Score waves form S = Q K^T and dP = dO V^T with K
+//   and V held in registers as B operands (the accumulator holds one key per lane and 16
+//   queries in its registers), then P and dS; accumulator waves add dV^T += dO^T P and
+//   dK^T += Q^T dS with the transposed operands read by ds_read_b64_tr_b16 and P / dS as the
+//   B operands (the register/key correspondence of the forward kernels, with the roles of
+//   queries and keys exchanged).
 // Scores stay in base-2 units (|scale| log2 e folded into one multiply); a negative scale
 // negates q exactly and dQ at the end. P and dS are rounded to bf16 for the MFMAs, with fp32
 // accumulation; the outputs are rounded to bf16 once.
@@ -106,28 +105,6 @@ __device__ __forceinline__ u32x4 read_tr(const uint16_t* tile, int c16, const Ti
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + to.tr[dt][1]));
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
   return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
-}
-
-// ---- delta_i = sum_c dO_ic O_ic ------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256)
-void bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, float* __restrict__ delta,
-                      long long rows) {
-  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const u32x4* orow = (const u32x4*)(o + r * D);
-  const u32x4* drow = (const u32x4*)(dout + r * D);
-  float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 x = orow[c], y = drow[c];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      s0 = fmaf(bf16_lo(x[t]), bf16_lo(y[t]), s0);
-      s1 = fmaf(bf16_hi(x[t]), bf16_hi(y[t]), s1);
-    }
-  }
-  delta[r] = s0 + s1;
 }
 
 // ---- dK, dV --------------------------------------------------------------------------------
@@ -436,7 +413,25 @@ void bwd_dq_kernel(BwdArgs a) {
     }
   }
   const float lse2 = a.lse[(size_t)bh * N + min(qi, N - 1)] * kLog2e;
-  const float dlt = a.delta[(size_t)bh * N + min(qi, N - 1)];
+  // delta_i = sum_c dO_ic O_ic: this lane holds half of the row's features (8hh .. 8hh+7 of
+  // every 16), the lane 32 apart the other half
+  float dlt;
+  {
+    const uint16_t* orow = (const uint16_t*)a.o + head + (size_t)min(qi, N - 1) * D;
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const u32x4 x = *(const u32x4*)(orow + 16 * kk + 8 * hh);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        s0 = fmaf(bf16_lo(x[t]), bf16_lo(df[kk][t]), s0);
+        s1 = fmaf(bf16_hi(x[t]), bf16_hi(df[kk][t]), s1);
+      }
+    }
+    const float part = s0 + s1;
+    dlt = part + __shfl_xor(part, 32);
+    if (hh == 0 && qi < N) a.delta[(size_t)bh * N + qi] = dlt;
+  }
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -536,12 +531,10 @@ void bwd_dq_kernel(BwdArgs a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  const long long rows = (long long)a.BH * a.N;
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
-                     (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
   const unsigned nblk = (unsigned)((a.N + NW * BLK - 1) / (NW * BLK));
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(DKDV_NT), 0, stream, a);
+  // dQ first: it writes delta, which the dK/dV kernel reads
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(DKDV_NT), 0, stream, a);
   return hipGetLastError();
 }
 

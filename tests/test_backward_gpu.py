@@ -79,3 +79,31 @@ def test_backward_medium():
     """Several key blocks and query blocks, both masks, end to end."""
     run_case(1, 4, 1024, 128, True, seed=2700, forward="gpu")
     run_case(1, 2, 1024, 64, False, seed=2701, forward="gpu")
+
+
+@pytest.mark.parametrize("d,N,causal", [(64, 77, False), (128, 300, True)])
+def test_backward_delta_workspace(d, N, causal):
+    """The delta workspace fa_bwd writes holds sum_c dO_ic O_ic per row (fp32 sum of exact
+    bf16 products: error at most a few units of 2^-24 times sum_c |dO_ic O_ic| per term)."""
+    import torch
+    import exact_softmax_attention_fa_amd as fa
+    B, H, seed = 2, 3, 2800 + d + N
+    scale = 1.0 / math.sqrt(d)
+    t = inputs.make_backward(B, H, N, d, seed)
+    q, k, v, dout = (to_device(t[x], "bf16") for x in ("q", "k", "v", "dout"))
+    note(f"backward delta B{B} H{H} N{N} d{d} causal={causal}")
+    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=q.device)
+    st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale,
+                   1 if causal else 0, torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK, fa.fa_status_string(st)
+    torch.cuda.synchronize()
+    o64 = o.double().cpu().numpy()
+    do64 = oracle.as_fp64(t["dout"], "bf16")
+    ref = oracle_bwd.delta(o64, do64)
+    bound = 2.0 ** -16 * np.abs(o64 * do64).sum(axis=-1) + 1e-30
+    got = delta.double().cpu().numpy()
+    assert np.all(np.isfinite(got)), "delta rows left unwritten"
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
