@@ -142,10 +142,12 @@ __device__ __forceinline__ void step_barrier() {
 //   P and dS (bf16, already in B-operand order) to their partner through LDS;
 // * accumulator waves (4..7) hold dK^T and dV^T of the same 32 keys and, one block later,
 //   add dO^T P and Q^T dS with the transposed operands read from the staged tiles.
-// Each role fits in half a SIMD's registers, so a score wave's softmax runs while its
-// partner on the same SIMD keeps the matrix core busy. The query blocks (Q and dO tiles,
-// log-normaliser and delta rows) rotate through four LDS slots, loaded straight from global
-// memory two blocks ahead: block j+2 loading, j+1 landed, j scored, j-1 accumulated.
+// Each role fits in half a SIMD's registers. A score wave is software-pipelined: while the
+// matrix core forms S and dP of block j+1, its VALU turns the S and dP of block j (held in
+// registers since the previous step) into P and dS, and the partner accumulates block j-1
+// meanwhile. The query blocks (Q and dO tiles, log-normaliser and delta rows) rotate through
+// five LDS slots, loaded straight from global memory two steps ahead of their first use:
+// block j+3 loading, j+2 landed, j+1 in the products, j waiting, j-1 accumulated.
 // P / dS rotate through two exchange buffers.
 constexpr int DKDV_NT = 2 * NT;          // 8 waves
 template <int D, bool CAUSAL>
@@ -154,7 +156,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int QT = BLK * D;           // swizzled Q / dO tile (elements)
   constexpr int TILEB = 2 * QT;         // bytes per tile
   constexpr int SLOTB = 2 * TILEB + 512;   // Q tile, dO tile, 64 floats of log-normaliser, 64 of delta
-  constexpr int SLOTS = 4;
+  constexpr int SLOTS = 5;
   constexpr int NC = D / 8;             // 16-byte chunks per row
   constexpr int IPW = D / 64;           // 1 KiB loads per wave per block (Q and dO: 2 TILEB)
   constexpr int KB_TILE = TILEB / 1024; // 1 KiB regions per tile
@@ -232,9 +234,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   const TileOffsets<D> to(lane);
-  // blocks qb0 and qb0+1 (a repeat of the last block when there is none) into slots 0 and 1
+  // blocks qb0 and qb0+1 (a repeat of the last block when there is none) into slots 0 and 1;
+  // step t (t = 0, 1, ...) issues block qb0+t+2 into slot (t+2) mod 5
   issue(qb0, 0);
   issue(min(qb0 + 1, nqb - 1), 1);
+  auto next_slot = [](int sl) { return sl == SLOTS - 1 ? 0 : sl + 1; };
 
   if (wave < NW) {
     // ---- score role ----
@@ -257,21 +261,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // the key operands are plain loads: wait for them before counting the block loads
     __builtin_amdgcn_s_waitcnt(0xc07f & ~0xc00f);   // vmcnt(0)
     barrier();   // block qb0 landed (qb0 + 1 may still be in flight)
-    for (int it = 0; it < nq; ++it) {
-      const int qb = qb0 + it;
-      issue(min(qb + 2, nqb - 1), (it + 2) & 3);
-      const uint16_t* Qs = (const uint16_t*)(smem + (it & 3) * SLOTB);
+
+    // S = Q K^T, dP = dO V^T of the block in slot sl: lane = key, register i = query
+    // 8(i/4) + 4hh + i%4
+    auto products = [&](int sl, f32x16& sc, f32x16& dp) __attribute__((always_inline)) {
+      const uint16_t* Qs = (const uint16_t*)(smem + sl * SLOTB);
       const uint16_t* dOs = Qs + QT;
-      const float* st = (const float*)(smem + (it & 3) * SLOTB + 2 * TILEB);
-      const int qf0 = qb * BLK;
-      f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l4[g] = *(const f32x4*)(st + 8 * g + 4 * hh);
-        d4[g] = *(const f32x4*)(st + 64 + 8 * g + 4 * hh);
-      }
-      // S = Q K^T, dP = dO V^T: lane = key, register i = query 8(i/4) + 4hh + i%4
-      f32x16 sc = {}, dp = {};
+      sc = (f32x16){};
+      dp = (f32x16){};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         const u32x4 qa = *(const u32x4*)(Qs + to.row[kk]);
@@ -279,22 +276,41 @@ void bwd_dkdv_kernel(BwdArgs a) {
         sc = mfma(qa, kf[kk], sc);
         dp = mfma(da, vf[kk], dp);
       }
-      const bool masked = (qf0 + BLK > N) || (kw0 + BLK > N) || (CAUSAL && qf0 < kw0 + BLK - 1);
+    };
+    // P and dS of block qb (statistics in slot sl: -lse log2 e and delta) into exchange
+    // buffer xb
+    auto softmax = [&](int qb, int sl, int xb, const f32x16& sc, const f32x16& dp) __attribute__((always_inline)) {
+      const float* st = (const float*)(smem + sl * SLOTB + 2 * TILEB);
+      const int qf0 = qb * BLK;
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l4[g] = *(const f32x4*)(st + 8 * g + 4 * hh);
+        d4[g] = *(const f32x4*)(st + 64 + 8 * g + 4 * hh);
+      }
       float p[16], ds[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int i = 4 * g + t;
-          float pv = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, -l4[g][t] * kLog2e));
-          if (masked) {
+        for (int t = 0; t < 4; ++t) p[4 * g + t] = __builtin_amdgcn_exp2f(fmaf(sc[4 * g + t], sl2, l4[g][t]));
+      // ragged or diagonal blocks only; the empty asm keeps this a branch rather than selects
+      // on every block
+      const bool masked = (qf0 + BLK > N) || (kw0 + BLK > N) || (CAUSAL && qf0 < kw0 + BLK - 1);
+      if (masked) {
+        asm volatile("");
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
             const int qi = qf0 + 8 * g + 4 * hh + t;
-            if (qi >= N || key >= N || (CAUSAL && key > qi)) pv = 0.0f;
+            if (qi >= N || key >= N || (CAUSAL && key > qi)) p[4 * g + t] = 0.0f;
           }
-          p[i] = pv;
-          ds[i] = pv * (dp[i] - d4[g][t]);
-        }
-      u32x4* xo = &xch[it & 1][pair][0][lane];
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ds[4 * g + t] = p[4 * g + t] * (dp[4 * g + t] - d4[g][t]);
+      u32x4* xo = &xch[xb][pair][0][lane];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         xo[64 * c] = (u32x4){pack_bf16x2(p[8 * c + 0], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
@@ -302,8 +318,32 @@ void bwd_dkdv_kernel(BwdArgs a) {
         xo[64 * (2 + c)] = (u32x4){pack_bf16x2(ds[8 * c + 0], ds[8 * c + 1]), pack_bf16x2(ds[8 * c + 2], ds[8 * c + 3]),
                                    pack_bf16x2(ds[8 * c + 4], ds[8 * c + 5]), pack_bf16x2(ds[8 * c + 6], ds[8 * c + 7])};
       }
-      barrier();   // block qb + 1 landed; P / dS of block qb visible
+    };
+
+    // step 0: products of block qb0
+    f32x16 sa, da, sb, db;
+    issue(min(qb0 + 2, nqb - 1), 2);
+    products(0, sa, da);
+    barrier();
+    // step t >= 1: products of block qb0+t (a repeat of the last block at t = nq, unused)
+    // beside the softmax of block qb0+t-1; unrolled by two so that the two register sets
+    // swap roles without copies
+    int sl_prev = 0, sl_cur = 1, sl_issue = 3;
+    auto step = [&](int it, const f32x16& sc, const f32x16& dp, f32x16& sc_n, f32x16& dp_n) __attribute__((always_inline)) {
+      issue(min(qb0 + it + 2, nqb - 1), sl_issue);
+      products(sl_cur, sc_n, dp_n);
+      softmax(qb0 + it - 1, sl_prev, (it - 1) & 1, sc, dp);
+      sl_prev = sl_cur;
+      sl_cur = next_slot(sl_cur);
+      sl_issue = next_slot(sl_issue);
+      barrier();   // block qb0+it+1 landed; P / dS of block qb0+it-1 visible
+    };
+    int it = 1;
+    for (; it + 1 <= nq; it += 2) {
+      step(it, sa, da, sb, db);
+      step(it + 1, sb, db, sa, da);
     }
+    if (it <= nq) step(it, sa, da, sb, db);
     barrier();     // the accumulators' last block
   } else {
     // ---- accumulator role ----
@@ -313,15 +353,31 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
 
+    // At step t the first accumulator wave turns the log-normalisers of block qb0+t (landed
+    // by then, read by the score waves' softmax at step t+1) into -lse log2 e in place.
+    auto prescale = [&](int sl) __attribute__((always_inline)) {
+      if (wave == NW) {
+        float* st = (float*)(smem + sl * SLOTB + 2 * TILEB);
+        st[lane] *= -kLog2e;
+      }
+    };
     barrier();   // block qb0 landed
-    // first step: the score waves take block qb0, nothing to accumulate yet
+    // steps 0 and 1: the score waves form block qb0's products and then its P / dS
     issue(min(qb0 + 2, nqb - 1), 2);
+    prescale(0);
     barrier();
-    for (int it = 1; it <= nq; ++it) {
-      issue(min(qb0 + it + 2, nqb - 1), (it + 2) & 3);
-      const uint16_t* Qs = (const uint16_t*)(smem + ((it - 1) & 3) * SLOTB);
+    issue(min(qb0 + 3, nqb - 1), 3);
+    prescale(1);
+    barrier();
+    // step t >= 2: accumulate block qb0+t-2
+    int sl_acc = 0, sl_issue = 4, sl_pre = 2;
+    for (int it = 2; it <= nq + 1; ++it) {
+      issue(min(qb0 + it + 2, nqb - 1), sl_issue);
+      prescale(sl_pre);
+      sl_pre = next_slot(sl_pre);
+      const uint16_t* Qs = (const uint16_t*)(smem + sl_acc * SLOTB);
       const uint16_t* dOs = Qs + QT;
-      const u32x4* xi = &xch[(it - 1) & 1][pair][0][lane];
+      const u32x4* xi = &xch[it & 1][pair][0][lane];
       u32x4 tq[D / 32][2], tdo[D / 32][2];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
@@ -340,6 +396,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
           dv[dt] = mfma(tdo[dt][c], pb[c], dv[dt]);
           dk[dt] = mfma(tq[dt][c], db[c], dk[dt]);
         }
+      sl_acc = next_slot(sl_acc);
+      sl_issue = next_slot(sl_issue);
       barrier();
     }
 
