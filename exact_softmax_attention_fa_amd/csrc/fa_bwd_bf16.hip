@@ -545,17 +545,22 @@ void bwd_dq_kernel(BwdArgs a) {
         s = mfma(ka, qf[kk], s);
         dp = mfma(va, df[kk], dp);
       }
-      const bool masked = (key0 + BLK > N) || (qi >= N) || (CAUSAL && key0 + BLK - 1 > qw0);
-      float ds[16];
+      float pv[16], ds[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2));
-        if (masked) {
+      for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2));
+      // ragged or diagonal tiles only; the empty asm keeps this a branch rather than selects
+      // on every tile
+      const bool masked = (key0 + BLK > N) || (qw0 + BLK > N) || (CAUSAL && key0 + BLK - 1 > qw0);
+      if (masked) {
+        asm volatile("");
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
           const int kj = key0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (kj >= N || qi >= N || (CAUSAL && kj > qi)) pv = 0.0f;
+          if (kj >= N || qi >= N || (CAUSAL && kj > qi)) pv[i] = 0.0f;
         }
-        ds[i] = pv * (dp[i] - dlt);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = pv[i] * (dp[i] - dlt);
       u32x4 db[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
