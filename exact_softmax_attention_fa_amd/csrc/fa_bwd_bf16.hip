@@ -161,8 +161,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int IPW = D / 64;           // 1 KiB loads per wave per block (Q and dO: 2 TILEB)
   constexpr int KB_TILE = TILEB / 1024; // 1 KiB regions per tile
   static_assert(2 * KB_TILE == 8 * IPW, "8 waves load the two tiles");
-  // vector-memory operations per block: the tiles, plus the row statistics on waves 0 and 1
-  constexpr int OPS_STAT = IPW + 1, OPS_TILE = IPW;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[SLOTS * SLOTB];
   __shared__ __attribute__((aligned(16))) u32x4 xch[2][NW][4][64];      // [buf][pair][pb0 pb1 db0 db1][lane]
@@ -193,44 +191,51 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = nqb - qb0;
 
   // ---- loads of one block into a slot -------------------------------------------------------
-  // Wave w fills 1 KiB regions w*IPW .. w*IPW+IPW-1 of the slot's two tiles: lane l writes
-  // physical chunk l % NC of row kb*(512/D) + l / NC, so it loads that row's logical chunk
-  // (physical ^ swz(row)). Rows past N repeat row N-1 (masked later). Waves 0 and 1 also load
-  // the block's 32 log-normalisers and deltas (lanes 32..63 repeat lanes 0..31).
+  // Only the score waves load, at the end of their step (they reach the barrier first).
+  // Score wave w fills the 1 KiB regions 2 IPW w .. 2 IPW w + 2 IPW - 1 of the slot's two
+  // tiles: lane l writes physical chunk l % NC of row kb*(512/D) + l / NC, so it loads that
+  // row's logical chunk (physical ^ swz(row)). Rows past N repeat row N-1 (masked later).
+  // Waves 0 and 1 also load the block's 32 log-normalisers and deltas (lanes 32..63 repeat
+  // lanes 0..31).
+  constexpr int RPW = 2 * IPW;          // regions per loading wave
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
-  const int tile_of_wave = (wave * IPW) / KB_TILE;       // 0: Q, 1: dO
+  const int lw = wave;                  // loading wave index (score waves)
+  const int tile_of_wave = (min(lw, NW - 1) * RPW) / KB_TILE;  // 0: Q, 1: dO
   const uint8_t* tile_src = (const uint8_t*)(tile_of_wave == 0 ? a.q : a.dout) + head * 2;
-  int dma_row[IPW];
-  uint32_t dma_off[IPW];
+  int dma_row[RPW];
+  uint32_t dma_off[RPW];
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int kb = (wave * IPW + i) % KB_TILE;
+  for (int i = 0; i < RPW; ++i) {
+    const int kb = (min(lw, NW - 1) * RPW + i) % KB_TILE;
     const int r = kb * (512 / D) + lane / NC;
     dma_row[i] = r;
     dma_off[i] = (uint32_t)(r * 2 * D + 16 * ((lane % NC) ^ swz<D>(r)));
   }
-  const float* stat_src = wave == 0 ? a.lse + (size_t)bh * N : a.delta + (size_t)bh * N;
+  const float* stat_src = lw == 0 ? a.lse + (size_t)bh * N : a.delta + (size_t)bh * N;
   auto issue = [&](int qb, int slot) __attribute__((always_inline)) {
+    if (wave >= NW) return;
     const int row0 = qb * BLK;
     const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(lds_base + (uint32_t)(slot * SLOTB + tile_of_wave * TILEB)));
     const uint8_t* src = tile_src + (size_t)row0 * 2 * D;
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
+    for (int i = 0; i < RPW; ++i) {
       const int over = row0 + dma_row[i] - (N - 1);
       const uint32_t back = over > 0 ? (uint32_t)over * 2u * D : 0u;
-      const int kb = (wave * IPW + i) % KB_TILE;
+      const int kb = (lw * RPW + i) % KB_TILE;
       dma16(src, dma_off[i] - back, dst + (uint32_t)(kb * 1024));
     }
-    if (wave < 2) {
+    if (lw < 2) {
       const uint32_t sdst = (uint32_t)__builtin_amdgcn_readfirstlane(
-          (int)(lds_base + (uint32_t)(slot * SLOTB + 2 * TILEB + wave * 256)));
+          (int)(lds_base + (uint32_t)(slot * SLOTB + 2 * TILEB + lw * 256)));
       dma4(stat_src + row0, (uint32_t)(4 * min(lr, N - 1 - row0)), sdst);
     }
   };
+  // vector-memory operations per block of a loading wave; the accumulators have none in flight
   auto barrier = [&]() __attribute__((always_inline)) {
-    if (wave < 2) step_barrier<OPS_STAT>();
-    else step_barrier<OPS_TILE>();
+    if (wave >= NW) step_barrier<0>();
+    else if (lw < 2) step_barrier<RPW + 1>();
+    else step_barrier<RPW>();
   };
 
   const TileOffsets<D> to(lane);
@@ -322,17 +327,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
     // step 0: products of block qb0
     f32x16 sa, da, sb, db;
-    issue(min(qb0 + 2, nqb - 1), 2);
     products(0, sa, da);
+    issue(min(qb0 + 2, nqb - 1), 2);
     barrier();
     // step t >= 1: products of block qb0+t (a repeat of the last block at t = nq, unused)
     // beside the softmax of block qb0+t-1; unrolled by two so that the two register sets
     // swap roles without copies
     int sl_prev = 0, sl_cur = 1, sl_issue = 3;
     auto step = [&](int it, const f32x16& sc, const f32x16& dp, f32x16& sc_n, f32x16& dp_n) __attribute__((always_inline)) {
-      issue(min(qb0 + it + 2, nqb - 1), sl_issue);
       products(sl_cur, sc_n, dp_n);
       softmax(qb0 + it - 1, sl_prev, (it - 1) & 1, sc, dp);
+      // block qb0+it+2 into the slot that block qb0+it-3 left (read by nobody since the last
+      // barrier)
+      issue(min(qb0 + it + 2, nqb - 1), sl_issue);
       sl_prev = sl_cur;
       sl_cur = next_slot(sl_cur);
       sl_issue = next_slot(sl_issue);
@@ -363,16 +370,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
     };
     barrier();   // block qb0 landed
     // steps 0 and 1: the score waves form block qb0's products and then its P / dS
-    issue(min(qb0 + 2, nqb - 1), 2);
     prescale(0);
     barrier();
-    issue(min(qb0 + 3, nqb - 1), 3);
     prescale(1);
     barrier();
     // step t >= 2: accumulate block qb0+t-2
-    int sl_acc = 0, sl_issue = 4, sl_pre = 2;
+    int sl_acc = 0, sl_pre = 2;
     for (int it = 2; it <= nq + 1; ++it) {
-      issue(min(qb0 + it + 2, nqb - 1), sl_issue);
       prescale(sl_pre);
       sl_pre = next_slot(sl_pre);
       const uint16_t* Qs = (const uint16_t*)(smem + sl_acc * SLOTB);
@@ -397,7 +401,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
           dk[dt] = mfma(tq[dt][c], db[c], dk[dt]);
         }
       sl_acc = next_slot(sl_acc);
-      sl_issue = next_slot(sl_issue);
       barrier();
     }
 
