@@ -7,6 +7,7 @@
 
 #include "fa.h"
 #include "fa_internal.h"
+#include "fa_bwd_internal.h"
 
 namespace {
 

@@ -30,7 +30,7 @@
 #include <stdint.h>
 #include <math.h>
 
-#include "fa_internal.h"
+#include "fa_bwd_internal.h"
 
 namespace fa {
 namespace {
