@@ -431,13 +431,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2)
 void bwd_dq_kernel(BwdArgs a) {
-  constexpr int KT = BLK * D;           // swizzled K / V tiles (elements)
-  constexpr int STAGE = 2 * KT;
-  constexpr int CH = BLK * D / 8;
-  static_assert(CH % NT == 0, "tile split");
-  constexpr int CPT = 2 * CH / NT;      // chunks per thread: the first half K, the rest V
+  // A step covers 64 keys, two sub-tiles of 32: slot = [K sub 0][K sub 1][V sub 0][V sub 1],
+  // each a swizzled [32][D] tile. Two slots: step t works on one while step t+1's keys land
+  // in the other, loaded straight from global memory at the start of step t.
+  constexpr int KT = BLK * D;           // one swizzled sub-tile (elements)
+  constexpr int SLOT = 4 * KT;          // elements per slot
+  constexpr int NC = D / 8;             // 16-byte chunks per row
+  constexpr int KB_SUB = 2 * KT / 1024; // 1 KiB regions per sub-tile: one wave loads one sub-tile
+  static_assert(KB_SUB * 1024 == 2 * KT, "sub-tile size");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -457,8 +460,6 @@ void bwd_dq_kernel(BwdArgs a) {
   const int qi = qw0 + lr;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ Qh = (const uint16_t*)a.q + head;
-  const uint16_t* __restrict__ Kh = (const uint16_t*)a.k + head;
-  const uint16_t* __restrict__ Vh = (const uint16_t*)a.v + head;
   const uint16_t* __restrict__ dOh = (const uint16_t*)a.dout + head;
 
   // Q'^T and dO^T as B operands (lane = query)
@@ -501,44 +502,50 @@ void bwd_dq_kernel(BwdArgs a) {
     for (int i = 0; i < 16; ++i) dq[dt][i] = 0.0f;
 
   const int kv_end = CAUSAL ? min(N, q0 + NW * BLK) : N;
-  const int nkt = (kv_end + BLK - 1) / BLK;
 
-  // Key rows past N repeat row N-1; their probabilities are masked to zero. The loaded
-  // registers are not touched before they are written to LDS (loads stay in flight).
-  u32x4 sreg[CPT];
-  auto gload = [&](int t) __attribute__((always_inline)) {
+  // Wave w loads sub-tile w % 2 of K (w < 2) or V (w >= 2): lane l writes physical chunk
+  // l % NC of row kb*(512/D) + l / NC of the sub-tile, i.e. that row's logical chunk
+  // (physical ^ swz(row)). Key rows past N repeat row N-1; their probabilities are masked.
+  // The per-lane offset is unsigned, so the base row is clamped to N-1 first: a sub-tile that
+  // starts past N then reads row N-1 throughout.
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
+  const uint8_t* ld_src = (const uint8_t*)(wave < 2 ? a.k : a.v) + head * 2;
+  int dma_row[KB_SUB];
+  uint32_t dma_off[KB_SUB];
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int cc = tid + (r % (CPT / 2)) * NT;
-      const int row = t * BLK + cc / (D / 8);
-      const int col = (cc % (D / 8)) * 8;
-      const uint16_t* src = r < CPT / 2 ? Kh : Vh;
-      sreg[r] = *(const u32x4*)(src + (size_t)min(row, N - 1) * D + col);
-    }
-  };
-  auto swrite = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* base = smem + buf * STAGE;
+  for (int i = 0; i < KB_SUB; ++i) {
+    const int r = i * (512 / D) + lane / NC;
+    dma_row[i] = r;
+    dma_off[i] = (uint32_t)(r * 2 * D + 16 * ((lane % NC) ^ swz<D>(r)));
+  }
+  auto issue = [&](int t, int slot) __attribute__((always_inline)) {
+    // first key of this wave's sub-tile, clamped so that every offset below is >= 0
+    const int row0 = min(2 * t * BLK + (wave & 1) * BLK, N - 1);
+    const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(lds_base + (uint32_t)(slot * SLOT * 2 + wave * KT * 2)));
+    const uint8_t* src = ld_src + (size_t)row0 * 2 * D;
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int cc = tid + (r % (CPT / 2)) * NT;
-      *(u32x4*)(base + (r < CPT / 2 ? 0 : KT) + tile_off<D>(cc / (D / 8), cc % (D / 8))) = sreg[r];
+    for (int i = 0; i < KB_SUB; ++i) {
+      const int over = row0 + dma_row[i] - (N - 1);   // rows past N-1 read row N-1
+      const uint32_t back = over > 0 ? (uint32_t)over * 2u * D : 0u;
+      dma16(src, dma_off[i] - back, dst + (uint32_t)(i * 1024));
     }
   };
 
   const TileOffsets<D> to(lane);
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  // Every wave takes every key tile: tiles past a wave's last query (causal) or waves past N
-  // see only masked probabilities and add zeros, which keeps the loop free of branches.
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    gload(min(t + 1, nkt - 1));
+  const int nst = (kv_end + 2 * BLK - 1) / (2 * BLK);   // 64-key steps
+  issue(0, 0);
+  step_barrier<0>();
+  // Every wave takes every key sub-tile: sub-tiles past a wave's last query (causal) or past
+  // N see only masked probabilities and add zeros, which keeps the loop free of branches.
+  for (int t = 0; t < nst; ++t) {
+    if (t + 1 < nst) issue(t + 1, (t + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* Ks = smem + buf * STAGE;
-    const uint16_t* Vs = Ks + KT;
-    const int key0 = t * BLK;
-    {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const uint16_t* Ks = smem + (t & 1) * SLOT + sub * KT;
+      const uint16_t* Vs = Ks + 2 * KT;
+      const int key0 = (2 * t + sub) * BLK;
       // S^T = K Q'^T, dP^T = V dO^T: lane = query, register i = key 8(i/4) + 4hh + i%4
       f32x16 s = {}, dp = {};
 #pragma unroll
@@ -551,8 +558,8 @@ void bwd_dq_kernel(BwdArgs a) {
       float pv[16], ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lse2));
-      // ragged or diagonal tiles only; the empty asm keeps this a branch rather than selects
-      // on every tile
+      // ragged or diagonal sub-tiles only; the empty asm keeps this a branch rather than
+      // selects on every sub-tile
       const bool masked = (key0 + BLK > N) || (qw0 + BLK > N) || (CAUSAL && key0 + BLK - 1 > qw0);
       if (masked) {
         asm volatile("");
@@ -575,8 +582,9 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) dq[dt] = mfma(read_tr<D>(Ks, c, to, dt), db[c], dq[dt]);
     }
-    swrite(buf ^ 1);
-    __syncthreads();
+    // the next step's keys have landed (each wave waits for its own loads) and nobody reads
+    // this step's slot any more
+    step_barrier<0>();
   }
 
   // dQ = scale * (dS K): |scale| from the accumulation, sign from the flipped q
