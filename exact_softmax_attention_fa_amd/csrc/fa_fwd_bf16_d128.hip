@@ -8,7 +8,7 @@
 // * 8 waves per workgroup, 32 query rows each (256 rows per workgroup), two waves per SIMD.
 //   The waves form two groups (waves 0-3 and 4-7, one wave of each group per SIMD) that run
 //   one phase apart. Every key tile j is handled in two phases per wave:
-//     M_j: S_j^T = K_j Q^T (16 MFMAs) and O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs)
+//     M_j: O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs), then S_j^T = K_j Q^T (16 MFMAs)
 //     V_j: online-softmax update of S_j into P_j (exponentials and the other VALU work)
 //   separated by workgroup barriers. While one group is in an M phase the other is in a V
 //   phase, so each SIMD keeps its matrix unit busy with one wave while the other wave's
@@ -21,6 +21,10 @@
 //   each row are XOR-swizzled: K chunk c of row r sits at c ^ (r & 15) (the 16-byte operand
 //   reads of 16 consecutive rows hit distinct banks), V chunk c at c ^ 4*(r & 3) (the
 //   transpose reads of 4 consecutive rows and two 16-feature halves hit distinct banks).
+// * Operand reads from LDS run a few MFMAs ahead. The first V^T operands of M_j are requested
+//   at the end of the wave's V_{j-1} phase (V_{j-1} has been in LDS since M_{j-1}) and the first
+//   K operands of S_j during the last steps of the V product, so that neither product of an M
+//   phase starts by waiting for LDS; LDS reads may stay in flight across the phase barriers.
 // * Operand layouts are those of the generic kernel: S^T and O^T accumulators hold one query
 //   per lane, probabilities go from the S^T accumulator into the B operand of the second
 //   product without data movement, and V^T operands come from ds_read_b64_tr_b16.
@@ -95,24 +99,28 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
 }
 
-// Wait until at most `n` vector-memory operations of this wave are outstanding and all of
-// its LDS reads have returned.
-template <int n>
-__device__ __forceinline__ void wait_vm_lgkm0() {
+// Wait until at most `n` vector-memory operations of this wave are outstanding and, with
+// LGKM = 0, all of its LDS reads have returned (LGKM = 15: LDS reads may stay in flight).
+template <int n, int LGKM = 0>
+__device__ __forceinline__ void wait_vm() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
+  static_assert(LGKM == 0 || LGKM == 15, "lgkmcnt: all or none");
   // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
-  constexpr int imm = (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14);
+  constexpr int imm = (n & 15) | (7 << 4) | (LGKM << 8) | ((n >> 4) << 14);
   __builtin_amdgcn_s_waitcnt(imm);
 }
 
 // Barrier between phases. `ahead` = how many tiles this wave has requested beyond the last
 // tile that some wave reads in the coming phase: the DMA loads of those tiles may stay in
-// flight, everything older must have landed in LDS. The compiler does not see the LDS
-// writes of the DMA loads, so the barrier is also a compiler memory barrier.
+// flight, everything older must have landed in LDS. LDS reads may stay in flight across it:
+// every read either feeds an MFMA of the phase it was issued in, or requests operands of the
+// wave's next M phase from a slot that no load overwrites before that phase has ended. The
+// compiler does not see the LDS writes of the DMA loads, so the barrier is also a compiler
+// memory barrier.
 __device__ __forceinline__ void phase_barrier(int ahead) {
-  if (ahead >= 2) wait_vm_lgkm0<2 * LOADS_PER_TILE>();
-  else if (ahead == 1) wait_vm_lgkm0<LOADS_PER_TILE>();
-  else wait_vm_lgkm0<0>();
+  if (ahead >= 2) wait_vm<2 * LOADS_PER_TILE, 15>();
+  else if (ahead == 1) wait_vm<LOADS_PER_TILE, 15>();
+  else wait_vm<0, 15>();
   asm volatile("s_barrier" ::: "memory");
 }
 
@@ -250,27 +258,53 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   if (grp == 1 && nkv > 2) issue_tile(2);
   phase_barrier(last_issued);
 
-  // S_j^T = K_j Q^T from LDS slot KS. Operand reads run PF steps ahead of the MFMAs;
-  // scheduling barriers keep the compiler from sinking them next to their uses.
+  // Operand reads run PF steps ahead of the MFMAs; scheduling barriers keep the compiler from
+  // sinking them next to their uses. The reads of one product's first PF steps are issued
+  // before it starts, in the preceding phase or product, so that no product waits for LDS at
+  // its start.
 #ifndef FA_PF
 #define FA_PF 3
 #endif
-  constexpr int PF = FA_PF;
-  auto s_product = [&](auto ks_tag) __attribute__((always_inline)) {
+#ifndef FA_PFV
+#define FA_PFV 3
+#endif
+  constexpr int PF = FA_PF;     // K operand steps in flight
+  constexpr int PFV = FA_PFV;   // V operand steps in flight (requested in the V phase before)
+  constexpr int S_STEPS = D / 16;                  // S^T = K Q^T: 8 steps of two MFMAs
+  constexpr int PV_STEPS = (BC / 16) * (D / 32);   // O^T += V^T P^T: 16 MFMAs
+  u32x4 kb0[S_STEPS], kb1[S_STEPS];   // K operands of the two 32-key blocks
+  u32x4 av[PV_STEPS];                 // V^T operands
+  auto k_load = [&](int kk, auto ks_tag) __attribute__((always_inline)) {
     constexpr uint32_t kslot = decltype(ks_tag)::value * TILEB;
-    constexpr int STEPS = D / 16;
-    u32x4 kb0[STEPS], kb1[STEPS];
-    auto load_step = [&](int kk) __attribute__((always_inline)) {
-      kb0[kk] = *(const lds_u32x4*)(uintptr_t)(koff[kk] + kslot);
-      kb1[kk] = *(const lds_u32x4*)(uintptr_t)(koff[kk] + (kslot + 32 * ROWB));
-    };
+    kb0[kk] = *(const lds_u32x4*)(uintptr_t)(koff[kk] + kslot);
+    kb1[kk] = *(const lds_u32x4*)(uintptr_t)(koff[kk] + (kslot + 32 * ROWB));
+  };
+  auto v_load = [&](int st, auto vs_tag) __attribute__((always_inline)) {
+    constexpr uint32_t vslot = decltype(vs_tag)::value * TILEB;
+    const int c16 = st / (D / 32), dt = st % (D / 32);
+    const uint32_t off = vslot + (uint32_t)(c16 * 16 * ROWB);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(voff[dt] + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(voff[dt] + (off + 8 * ROWB)));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+    av[st] = (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
+  };
+  auto k_prefetch = [&](auto ks_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < PF; ++kk) load_step(kk);
+    for (int kk = 0; kk < PF; ++kk) k_load(kk, ks_tag);
+  };
+  auto v_prefetch = [&](auto vs_tag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < PFV; ++st) v_load(st, vs_tag);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // S_j^T = K_j Q^T from LDS slot KS (first PF steps already requested).
+  auto s_product = [&](auto ks_tag) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     f32x16 c0 = {}, c1 = {};
 #pragma unroll
-    for (int kk = 0; kk < STEPS; ++kk) {
-      if (kk + PF < STEPS) load_step(kk + PF);
+    for (int kk = 0; kk < S_STEPS; ++kk) {
+      if (kk + PF < S_STEPS) k_load(kk + PF, ks_tag);
       __builtin_amdgcn_sched_barrier(0);
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kb0[kk]),
                                                    __builtin_bit_cast(bf16x8, qf[kk]), c0, 0, 0, 0);
@@ -282,25 +316,13 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
     s1 = c1;
   };
 
-  // O^T += V^T P^T from LDS slot VS: 16 MFMAs over (16-key chunk, 32-feature block).
-  auto pv_product = [&](auto vs_tag) __attribute__((always_inline)) {
-    constexpr uint32_t vslot = decltype(vs_tag)::value * TILEB;
-    constexpr int STEPS = (BC / 16) * (D / 32);
-    u32x4 av[STEPS];
-    auto load_step = [&](int st) __attribute__((always_inline)) {
-      const int c16 = st / (D / 32), dt = st % (D / 32);
-      const uint32_t off = vslot + (uint32_t)(c16 * 16 * ROWB);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(voff[dt] + off));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(voff[dt] + (off + 8 * ROWB)));
-      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-      av[st] = (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
-    };
+  // O^T += V^T P^T from LDS slot VS (first PF steps already requested); its last steps request
+  // the first K operands of the S product that follows, from slot KS.
+  auto pv_product = [&](auto vs_tag, auto ks_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int st = 0; st < PF; ++st) load_step(st);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      if (st + PF < STEPS) load_step(st + PF);
+    for (int st = 0; st < PV_STEPS; ++st) {
+      if (st + PFV < PV_STEPS) v_load(st + PFV, vs_tag);
+      else if (st + PF >= PV_STEPS) k_load(st + PF - PV_STEPS, ks_tag);
       __builtin_amdgcn_sched_barrier(0);
       const int c16 = st / (D / 32), dt = st % (D / 32);
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[st]),
@@ -310,13 +332,21 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   };
 
   // M phase of tile j held in LDS slot SLOT (j may equal nkv: then only the product with
-  // V_{j-1} remains). The wave raises its issue priority so that the other wave's vector
-  // work on the same SIMD does not hold back its MFMA stream.
-  auto m_phase = [&](int j, auto slot_tag) __attribute__((always_inline)) {
+  // V_{j-1} remains): first O^T += V_{j-1}^T P_{j-1}^T (its V operands were requested at the
+  // end of the wave's previous V phase; V_{j-1} has been in LDS since before M_{j-1}), then
+  // S_j. Tile 0 (FIRST) has only S_0. The wave raises its issue priority so that the other
+  // wave's vector work on the same SIMD does not hold back its MFMA stream.
+  auto m_phase = [&](int j, auto slot_tag, auto first_tag) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value != 0;
     __builtin_amdgcn_s_setprio(2);
-    if (j < nkv && j <= j_last) s_product(IntC<SL>{});
-    if (j >= 1 && j - 1 <= j_last) pv_product(IntC<(SL + SLOTS - 1) % SLOTS>{});
+    if constexpr (FIRST) {
+      k_prefetch(IntC<SL>{});
+      s_product(IntC<SL>{});
+    } else if (j - 1 <= j_last) {   // otherwise j > j_last as well: nothing left for this wave
+      pv_product(IntC<(SL + SLOTS - 1) % SLOTS>{}, IntC<SL>{});
+      if (j < nkv && j <= j_last) s_product(IntC<SL>{});
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -326,7 +356,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // whose reference is a huge negative number): then the tile maximum is found, the
   // denominator and numerator are rescaled and the exponentials are recomputed. Otherwise
   // every probability is at most 2^64, so the fp32 sums and bf16 probabilities stay finite.
-  auto v_phase = [&](int j) __attribute__((always_inline)) {
+  auto v_phase = [&](int j, auto slot_tag) __attribute__((always_inline)) {
     if (j > j_last) return;
     const int key0 = j * BC;
     const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq_lo);
@@ -375,6 +405,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
       pb[c] = w;
     }
     l_run += ls;
+    v_prefetch(slot_tag);   // V_j operands of the next M phase (tile j has been in LDS since M_j)
   };
 
   // Phases: M_0 V_0 M_1 V_1 ... M_{n-1} V_{n-1} M_n, one barrier after each. Group 1 starts
@@ -383,31 +414,33 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // the ring size so that every LDS slot offset is an immediate.
   const int lag = grp;   // interval of this wave's M_0
   if (grp == 1) barrier_after(0);
-  auto tile = [&](int j, auto slot_tag) __attribute__((always_inline)) {
-    m_phase(j, slot_tag);
+  auto tile = [&](int j, auto slot_tag, auto first_tag) __attribute__((always_inline)) {
+    m_phase(j, slot_tag, first_tag);
     barrier_after(2 * j + lag);
     if (j + 2 + grp < nkv) issue_tile(j + 2 + grp);
-    v_phase(j);
+    v_phase(j, slot_tag);
     barrier_after(2 * j + 1 + lag);
   };
-  int j = 0;
+  // Tile 0 (slot 0) is peeled off; the loop then runs tiles 1, 2, 3, 0 (mod 4) per iteration.
+  tile(0, IntC<0>{}, IntC<1>{});
+  int j = 1;
   for (; j + SLOTS <= nkv; j += SLOTS) {
-    tile(j, IntC<0>{});
-    tile(j + 1, IntC<1>{});
-    tile(j + 2, IntC<2>{});
-    tile(j + 3, IntC<3>{});
+    tile(j, IntC<1>{}, IntC<0>{});
+    tile(j + 1, IntC<2>{}, IntC<0>{});
+    tile(j + 2, IntC<3>{}, IntC<0>{});
+    tile(j + 3, IntC<0>{}, IntC<0>{});
   }
-  if (j < nkv) tile(j++, IntC<0>{});
-  if (j < nkv) tile(j++, IntC<1>{});
-  if (j < nkv) tile(j++, IntC<2>{});
+  if (j < nkv) tile(j++, IntC<1>{}, IntC<0>{});
+  if (j < nkv) tile(j++, IntC<2>{}, IntC<0>{});
+  if (j < nkv) tile(j++, IntC<3>{}, IntC<0>{});
   switch (nkv & (SLOTS - 1)) {   // the final M phase (product with V_{nkv-1} only)
-    case 0: m_phase(nkv, IntC<0>{}); break;
-    case 1: m_phase(nkv, IntC<1>{}); break;
-    case 2: m_phase(nkv, IntC<2>{}); break;
-    default: m_phase(nkv, IntC<3>{}); break;
+    case 0: m_phase(nkv, IntC<0>{}, IntC<0>{}); break;
+    case 1: m_phase(nkv, IntC<1>{}, IntC<0>{}); break;
+    case 2: m_phase(nkv, IntC<2>{}, IntC<0>{}); break;
+    default: m_phase(nkv, IntC<3>{}, IntC<0>{}); break;
   }
   if (grp == 0) barrier_after(2 * nkv);
-  wait_vm_lgkm0<0>();
+  wait_vm<0>();
 
   // ---- epilogue: o = u / l, lse = (m + log2 l) * ln 2 -----------------------------------------
   const float l_tot = pair_sum(l_run);
