@@ -267,7 +267,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(each GPU would run the same kernel on its own heads). Use --gpus 1.", file=sys.stderr)
         return 2
 
