@@ -50,6 +50,24 @@ def test_causal_medium_full(causal):
     full_parity(t, "bf16", 1 / math.sqrt(128), causal, f"n777 causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_late_keys_far_above_the_running_max(d, causal):
+    """Keys whose logits lie far above every earlier score arrive in later tiles (a raise of
+    the exponent reference after the first tile, twice, the second by 100 in natural units):
+    every query that sees them puts its weight there. Logit offsets come from a constant last
+    query coordinate, as in the boosted-key workload."""
+    N, scale = 700, 1.0 / math.sqrt(d)
+    t = inputs.make_random(1, 2, N, d, "bf16", seed=77)
+    q, k = t["q"].copy(), t["k"].copy()
+    q[..., d - 1] = inputs.f32_to_bf16_bits(np.float32(1.0))
+    k[..., d - 1] = 0
+    for key, logit in ((210, 50.0), (610, 100.0)):
+        k[:, :, key, d - 1] = inputs.f32_to_bf16_bits(np.float32(logit / scale))
+    t = {"q": q, "k": k, "v": t["v"]}
+    full_parity(t, "bf16", scale, causal, f"late spikes d{d} causal={causal}")
+
+
 # ---- scalar examples through fp32 (d = 1, scale = 1) ----------------------------------------
 
 def test_scalar_three_scores():
