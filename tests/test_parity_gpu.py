@@ -68,6 +68,29 @@ def test_late_keys_far_above_the_running_max(d, causal):
     full_parity(t, "bf16", scale, causal, f"late spikes d{d} causal={causal}")
 
 
+def _sweep_case(i: int):
+    """Seeded random case i: batch, heads, sequence length, head width, dtype, mask and scale."""
+    rng = np.random.default_rng(7000 + i)
+    dtype = "bf16" if i % 3 else "f32"
+    d = int(rng.choice([64, 128, 64, 128, int(rng.integers(1, 257))]))
+    N = int(rng.integers(1, 701))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    causal = bool(rng.integers(0, 2))
+    scale = float(rng.choice([1.0 / math.sqrt(d), rng.uniform(-0.3, 0.3)]))
+    return B, H, N, d, dtype, causal, scale
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shape_sweep(i):
+    """24 seeded random shapes over every kernel (d up to 256, ragged N, both masks and dtypes,
+    scales of either sign), each compared in full with the oracle."""
+    B, H, N, d, dtype, causal, scale = _sweep_case(i)
+    t = inputs.make_random(B, H, N, d, dtype, seed=8000 + i)
+    # fp32 logits larger than at 1/sqrt(d): the bound derived from fp32 rounding of the dot products
+    tol = fp32_logit_bound(t, scale) if (dtype == "f32" and abs(scale) > 1.0 / math.sqrt(d) + 1e-12) else None
+    full_parity(t, dtype, scale, causal, f"sweep {i}: B{B} H{H} N{N} d{d} {dtype} causal={causal} scale={scale:.4f}", tol)
+
+
 # ---- scalar examples through fp32 (d = 1, scale = 1) ----------------------------------------
 
 def test_scalar_three_scores():
