@@ -322,7 +322,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
 #pragma unroll
     for (int st = 0; st < PV_STEPS; ++st) {
       if (st + PFV < PV_STEPS) v_load(st + PFV, vs_tag);
-      else if (st + PF >= PV_STEPS) k_load(st + PF - PV_STEPS, ks_tag);
+      if (st + PF >= PV_STEPS) k_load(st + PF - PV_STEPS, ks_tag);
       __builtin_amdgcn_sched_barrier(0);
       const int c16 = st / (D / 32), dt = st % (D / 32);
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[st]),
