@@ -31,10 +31,18 @@ def test_bf16_b2_h8_n1024_full():
 @pytest.mark.parametrize("name,rows", [
     ("fwd_bf16_b4_h16_n4096_d128_causal", 24),
     ("fwd_bf16_b1_h16_n8192_d128_widek", 64),
-    ("fwd_bf16_b1_h8_n32768_d128_causal", 96),
+    ("fwd_bf16_b1_h8_n32768_d128_causal", 256),
 ])
 def test_full_size_sampled_rows(name, rows):
     sampled_parity(W[name], rows, name)
+
+
+@pytest.mark.parametrize("name", ["fwd_bf16_b4_h16_n4096_d128_causal", "fwd_bf16_b1_h16_n8192_d128_widek"])
+def test_full_size_every_row(name):
+    """The N = 4096 causal and the headline workloads compared with the oracle on every query
+    row of every head (the oracle takes seconds to tens of seconds on the host)."""
+    w = W[name]
+    full_parity(inputs.make(w), w.dtype, w.resolved_scale(), w.causal, f"every row {name}")
 
 
 def test_widek_small_full():
