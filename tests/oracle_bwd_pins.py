@@ -121,6 +121,21 @@ def pin_delta_identity(att, bwd):
             assert np.allclose(dl[0, h], (p * dp).sum(axis=1), rtol=0, atol=1e-13)
 
 
+def pin_sampled_matches_full(att, bwd):
+    """gradients_sampled (dQ rows from their own rows of P; dK and dV rows from the columns of P
+    and dS, built from the forward's lse and the delta identity) equals the full gradients on
+    the selected rows, both masks."""
+    q, k, v, do = _rand(81, 2, 2, 37, 5)
+    qr = np.array([0, 5, 17, 36])
+    kr = np.array([0, 1, 20, 36])
+    for causal in (False, True):
+        dq, dk, dv = bwd.gradients(q, k, v, do, 0.7, causal)
+        sq, sk, sv = bwd.gradients_sampled(q, k, v, do, 0.7, causal, qr, kr)
+        assert np.allclose(sq, dq[:, :, qr], rtol=0, atol=1e-12)
+        assert np.allclose(sk, dk[:, :, kr], rtol=0, atol=1e-12)
+        assert np.allclose(sv, dv[:, :, kr], rtol=0, atol=1e-12)
+
+
 PINS = {name[4:]: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}
 
 

@@ -107,3 +107,26 @@ def test_backward_delta_workspace(d, N, causal):
     got = delta.double().cpu().numpy()
     assert np.all(np.isfinite(got)), "delta rows left unwritten"
     assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+
+
+@pytest.mark.parametrize("B,H,N,causal", [(1, 16, 8192, False), (4, 16, 4096, True)])
+def test_backward_full_size_sampled(B, H, N, causal):
+    """The backward pass at the headline shape and at the N = 4096 causal shape (d = 128), on
+    fa_fwd's own o and lse, against the oracle on sampled query rows of dQ and sampled keys of
+    dK and dV (tile edges, the middle, the last row and seeded rows), which the oracle computes
+    row by row and column by column."""
+    import torch
+    import exact_softmax_attention_fa_amd as fa
+    d = 128
+    scale = 1.0 / math.sqrt(d)
+    t = inputs.make_backward(B, H, N, d, seed=9100 + N)
+    q, k, v, dout = (to_device(t[x], "bf16") for x in ("q", "k", "v", "dout"))
+    note(f"backward full size B{B} H{H} N{N} d{d} causal={causal}")
+    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, dout, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(N, 24, seed=9200 + N)
+    q64, k64, v64, do64 = (oracle.as_fp64(t[x], "bf16") for x in ("q", "k", "v", "dout"))
+    sq, sk, sv = oracle_bwd.gradients_sampled(q64, k64, v64, do64, scale, causal, rows, rows)
+    for name, g, r in (("dq", dq, sq), ("dk", dk, sk), ("dv", dv, sv)):
+        check(g[:, :, rows].double().cpu().numpy(), r, f"{name} full size B{B} H{H} N{N} causal={causal}")

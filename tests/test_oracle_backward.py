@@ -30,6 +30,11 @@ MUTANTS = [
     ("p = probabilities(qb, kb, scale, causal, rr)", "p = probabilities(qb, kb, scale, False, rr)",
      "mask ignored"),
     ("return (o * do).sum(axis=-1)", "return (o * do).sum(axis=-2)", "delta summed over rows"),
+    ("ds_cols = p_cols * (dp_cols - dlt[b, h][:, None])", "ds_cols = p_cols * dp_cols",
+     "sampled dK: row term dropped"),
+    ("p_cols = np.exp(s_cols - lse[b, h][:, None])", "p_cols = np.exp(s_cols)", "sampled columns: lse not subtracted"),
+    ("s_cols = np.where(k_rows[None, :] > np.arange(N)[:, None], -np.inf, s_cols)",
+     "s_cols = np.where(k_rows[None, :] < np.arange(N)[:, None], -np.inf, s_cols)", "sampled columns: mask reversed"),
 ]
 
 
@@ -37,7 +42,8 @@ def _load(src):
     mod = types.ModuleType("bwd_m")
     mod.__file__ = os.path.join(ROOT, "oracle", "backward.py")
     mod.__dict__["probabilities"] = att.probabilities
-    src = src.replace("from .attention import probabilities\n", "")
+    mod.__dict__["attention"] = att.attention
+    src = src.replace("from .attention import attention, probabilities\n", "")
     exec(compile(src, mod.__file__, "exec"), mod.__dict__)
     return mod
 
