@@ -57,9 +57,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max rises by > 2^8
 
-// Workgroups the key split aims for (a split doubles them while they stay at or below this).
-#ifndef FA_SPLIT_TARGET_WGS
-#define FA_SPLIT_TARGET_WGS 512
+// Largest grid (workgroups) that gets a key split: one workgroup per CU of the 256, so that a
+// split workgroup only needs room for its own waves.
+#ifndef FA_SPLIT_MAX_WGS
+#define FA_SPLIT_MAX_WGS 256
 #endif
 
 // Tile configuration per padded head width: QW query blocks of 32 per wave, NW waves per
@@ -509,14 +510,14 @@ hipError_t launch_split(const FwdArgs& a, bool fulld, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Key groups per workgroup: split the key range when the grid alone leaves most compute
-// units idle and every group still gets at least two tiles.
+// Key groups per workgroup: split the key range as far as MAXSPLIT allows when the grid has
+// at most one workgroup per CU, as long as every group still gets at least two tiles.
 template <int D>
 int choose_split(const FwdArgs& a) {
   const long long wgs = (long long)a.BH * a.n_qtiles;
   const int nkv = (a.N + Cfg<D>::BC - 1) / Cfg<D>::BC;
   int split = 1;
-  while (split * 2 <= Cfg<D>::MAXSPLIT && wgs * split * 2 <= FA_SPLIT_TARGET_WGS && nkv >= 2 * split * 2) split *= 2;
+  while (split * 2 <= Cfg<D>::MAXSPLIT && wgs <= FA_SPLIT_MAX_WGS && nkv >= 2 * split * 2) split *= 2;
   return split;
 }
 
