@@ -5,6 +5,7 @@ One step = one call of the C-ABI entry point over the whole workload (every quer
 every (b, h)), with q/k/v already resident in device memory. Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1] [--settle-s S]
+                  [--entry fwd|splitkv [--num-splits S]] [--naive] [--backward] [--launch-loop C]
 
 Before the W warm-up steps, untimed calls run for S seconds (default 0.2) so that the timed K
 steps see the clock the chip sustains under load rather than its ramp-up.
@@ -64,6 +65,31 @@ def kernel_hash(w: inputs.Workload) -> str:
     return h.hexdigest()[:16]
 
 
+def library_info() -> dict:
+    """The library file this process loads: its path, the sha256 of its bytes (first 16 hex
+    digits) and whether it is the in-tree product build or a FA_LIBRARY override."""
+    import exact_softmax_attention_fa_amd as fa
+    path = fa.library_path()
+    with open(path, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    override = "FA_LIBRARY" in os.environ
+    info = {"sha16": sha, "product": not override}
+    if override:
+        info["path"] = path
+    return info
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -89,6 +115,7 @@ def cpu_baseline(w: inputs.Workload, t: dict, rows_per_head: int) -> dict:
     keys = (rows + 1) if w.causal else np.full(len(rows), w.N)
     flops = 4.0 * w.d * float(keys.sum()) * w.B * w.H
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{len(rows)} of {w.N} query rows (evenly spaced) in each of {w.B * w.H} heads, "
                       f"fp64 numpy, {dt:.1f} s; flops counted per row as 4*d*visible keys"}
 
@@ -105,42 +132,60 @@ def copy_calibration(mib: int, steps: int) -> None:
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
 
 
-def naive_attention(q, k, v, scale: float, causal: bool, mask=None):
+def naive_attention(q, kt, v, scale: float, causal: bool, mask=None):
     """Standard (unfused) attention as the pages describe it before FlashAttention: the N x N
     score matrix and the probability matrix are both written to and read back from HBM
     (sadullah.online, "Standard attention"; lihaoran.work, the intermediate matrix).
-    Library GEMMs and a softmax kernel; a comparison only, never the product path."""
+    Library GEMMs and a softmax kernel; a comparison only, never the product path.
+
+    q, v: [B, H, N, d]; kt: K transposed to [B, H, d, N], contiguous (made once by the caller:
+    a batched bf16 product with a transposed view as right operand is avoided). The scores are
+    produced in fp32 (a bf16 x bf16 -> fp32 GEMM for bf16 inputs), as the fused kernel keeps
+    them; the probabilities are rounded to the input dtype before the product with V, as the
+    fused kernel rounds them."""
     import torch
-    s = torch.matmul(q, k.transpose(-1, -2).contiguous())   # [B, H, N, N], input dtype
-    s = s.float().mul_(scale)
+    B, H, N, d = q.shape
+    q3, kt3, v3 = q.reshape(B * H, N, d), kt.reshape(B * H, d, N), v.reshape(B * H, N, d)
+    if q.dtype == torch.bfloat16:
+        s = torch.bmm(q3, kt3, out_dtype=torch.float32)   # [B*H, N, N] fp32 in HBM
+    else:
+        s = torch.bmm(q3, kt3)
+    s.mul_(scale)
     if causal:
         s.masked_fill_(mask, float("-inf"))
-    p = torch.softmax(s, dim=-1).to(q.dtype)
-    return torch.matmul(p, v)
+    p = torch.softmax(s, dim=-1).to(q.dtype)                  # [B*H, N, N] in HBM
+    return torch.bmm(p, v3).reshape(B, H, N, d)
+
+
+# Largest |naive - fused| the comparison is expected to show: both sides meet the oracle's
+# bf16 bound (2e-2) or fp32 bound (1e-5), so they differ by at most twice that.
+NAIVE_AGREEMENT = {"bf16": 4e-2, "f32": 2e-5}
 
 
 def run_naive(w: inputs.Workload, q, k, v, o_fused, steps: int, warmup: int) -> dict:
-    """Times the unfused comparison on the same device inputs (events over the timed region)."""
+    """Times the unfused comparison on the same device inputs (events over the timed region).
+    The transposed copy of K is made once, before the timed region."""
     import torch
     mask = None
     if w.causal:
         mask = torch.ones(w.N, w.N, dtype=torch.bool, device=q.device).triu_(1)
     scale = w.resolved_scale()
+    kt = k.transpose(-1, -2).contiguous()
     for _ in range(warmup):
-        o = naive_attention(q, k, v, scale, w.causal, mask)
+        o = naive_attention(q, kt, v, scale, w.causal, mask)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(steps):
-        o = naive_attention(q, k, v, scale, w.causal, mask)
+        o = naive_attention(q, kt, v, scale, w.causal, mask)
     ev1.record(stream)
     torch.cuda.synchronize()
     t = ev0.elapsed_time(ev1) / steps / 1e3
     diff = (o.float() - o_fused.float()).abs().max().item()
     return {"value": round(w.flops / t / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(t * 1e3, 4),
-            "kind": "naive: matmul, softmax, matmul with the N x N matrices in HBM (torch)",
-            "max_abs_diff_vs_fused": diff}
+            "kind": "naive: bmm (fp32 scores), softmax, bmm with the N x N matrices in HBM (torch)",
+            "max_abs_diff_vs_fused": diff, "agrees_with_fused": diff <= NAIVE_AGREEMENT[w.dtype]}
 
 
 def run_backward(w: inputs.Workload, q, k, v, o, lse, steps: int, warmup: int) -> dict:
@@ -254,6 +299,11 @@ def main() -> int:
                          "(the clock ramps up over the first tens of milliseconds)")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows per head for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--entry", default="fwd", choices=["fwd", "splitkv"],
+                    help="entry point timed: the single-pass fa_fwd / fa_fwd_f32 (default) or "
+                         "fa_fwd_splitkv (key range split over workgroups, then a merge)")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="split columns requested from fa_fwd_splitkv (0 = the library's choice)")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (fa_bwd) on the forward's outputs")
     ap.add_argument("--naive", action="store_true",
@@ -293,10 +343,27 @@ def main() -> int:
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    entry = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
-    def make_args(stream_handle):
-        return (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                w.B, w.H, w.N, w.d, w.resolved_scale(), 1 if w.causal else 0, stream_handle)
+    split_info = None
+    if args.entry == "splitkv":
+        dtype_code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+        st, nsplit, ws_bytes = fa.fa_fwd_splitkv_plan(w.B, w.H, w.N, w.d, dtype_code, 1 if w.causal else 0,
+                                                      args.num_splits)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, "fa_fwd_splitkv_plan")
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)   # allocated before timing
+        split_info = {"requested": args.num_splits, "columns": nsplit, "workspace_bytes": ws_bytes}
+        entry = fa.fa_fwd_splitkv
+
+        def make_args(stream_handle):
+            return (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    w.B, w.H, w.N, w.d, w.resolved_scale(), 1 if w.causal else 0, dtype_code, args.num_splits,
+                    ws.data_ptr(), ws_bytes, stream_handle)
+    else:
+        entry = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+
+        def make_args(stream_handle):
+            return (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    w.B, w.H, w.N, w.d, w.resolved_scale(), 1 if w.causal else 0, stream_handle)
     call_args = make_args(stream.cuda_stream)
 
     def step():
@@ -336,8 +403,11 @@ def main() -> int:
     achieved = w.flops / avg_kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     kh = kernel_hash(w)
+    lib = library_info()
     traffic = TRAFFIC.get(w.name)
-    traffic_bytes = traffic["bytes"] if traffic and traffic.get("kernel_hash") == kh else None
+    # stored counters hold only for the product build of the sources they were taken on
+    traffic_bytes = (traffic["bytes"] if traffic and traffic.get("kernel_hash") == kh and lib["product"]
+                     and args.entry == "fwd" else None)
 
     line = {
         "metric": "fwd attention TFLOP/s (4BHN^2d), bf16 N=8192 d=128; % of MFMA peak",
@@ -363,8 +433,15 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes,
                      "hbm_gbs_algorithmic": round(w.algorithmic_bytes / avg_kernel_s / 1e9, 1),
                      "kernel_hash": kh},
+        "library": lib,
+        "entry": entry.__name__,
         "cpu_baseline": None,
     }
+    if split_info is not None:
+        line["splitkv"] = split_info
+        line["roofline"]["note"] = "kernel_avg_us covers both kernels of the call (partial pass and merge)"
+    if not lib["product"]:
+        line["non_product"] = "FA_LIBRARY override: not the in-tree build of the committed sources"
     if args.backward:
         line["backward"] = run_backward(w, q, k, v, o, lse, args.steps, args.warmup)
     if args.launch_loop > 0:

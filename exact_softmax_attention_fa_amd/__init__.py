@@ -7,10 +7,14 @@ kernels. PyTorch supplies device memory and the stream.
 Entry points with the C names:
   fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> status   (bf16, raw pointers)
   fa_fwd_f32(...)                                              -> status   (fp32, raw pointers)
+  fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, workspace,
+                 workspace_bytes, stream)                      -> status   (key range split)
+  fa_fwd_splitkv_plan(B, H, N, d, dtype, causal, num_splits)   -> (status, nsplit, workspace bytes)
   fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream) -> status
   fa_status_string(status)                                     -> str
 and tensor-level conveniences:
   fwd(q, k, v, scale=None, causal=False) -> (o, lse)
+  fwd_splitkv(q, k, v, scale=None, causal=False, num_splits=0) -> (o, lse)
   bwd(q, k, v, o, lse, dout, scale=None, causal=False) -> (dq, dk, dv)
 If the library has not been built, every call raises RuntimeError; there is no fallback.
 """
@@ -20,10 +24,12 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_status_string", "fwd", "bwd", "library_path", "load_library",
-           "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FaError"]
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_plan", "fa_bwd", "fa_status_string",
+           "fwd", "fwd_splitkv", "bwd", "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG",
+           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_BF16", "FA_F32", "FaError"]
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+FA_BF16, FA_F32 = 0, 1
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -48,6 +54,11 @@ def load_library():
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library not built: {path} is missing "
                            "(build it with `python -m exact_softmax_attention_fa_amd.build`)")
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7). Loading torch
+    # first makes the library bind to that runtime, the one that owns torch's memory and
+    # streams; loaded the other way round, the process would hold two HIP runtimes and every
+    # launch on a torch stream would fail.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
@@ -59,6 +70,12 @@ def load_library():
     lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                                                                           ctypes.c_void_p]
     lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = argtypes[:11] + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                                   ctypes.c_void_p]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_plan.argtypes = [ctypes.c_int] * 7 + [ctypes.POINTER(ctypes.c_int),
+                                                             ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_fwd_splitkv_plan.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -73,6 +90,21 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
 def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
     """fp32 forward on raw device pointers (ints); returns the C status code."""
     return load_library().fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, workspace, workspace_bytes,
+                   stream) -> int:
+    """Split-KV forward on raw device pointers (ints); returns the C status code."""
+    return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, workspace,
+                                         workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_plan(B, H, N, d, dtype, causal, num_splits):
+    """Host-only plan of a split-KV call: (status, split columns, workspace bytes)."""
+    ns, wb = ctypes.c_int(0), ctypes.c_size_t(0)
+    st = load_library().fa_fwd_splitkv_plan(B, H, N, d, dtype, causal, num_splits, ctypes.byref(ns),
+                                            ctypes.byref(wb))
+    return st, ns.value, wb.value
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream) -> int:
@@ -125,6 +157,44 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
             B, H, N, d, float(scale), 1 if causal else 0, handle)
     if st != FA_OK:
         raise FaError(st, fn.__name__)
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_splits: int = 0, workspace=None,
+                stream=None):
+    """Attention forward through the split-KV entry point (key range split over workgroups, then
+    a merge). Same tensors and result as ``fwd``; returns (o, lse). The workspace (uint8 device
+    tensor) is allocated with torch when not given; it must hold the bytes the plan reports."""
+    import torch
+
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B,H,N,d] shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dtype = FA_BF16 if q.dtype == torch.bfloat16 else FA_F32
+    st, _, need = fa_fwd_splitkv_plan(B, H, N, d, dtype, 1 if causal else 0, num_splits)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv_plan")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                        float(scale), 1 if causal else 0, dtype, num_splits, ws_ptr, ws_bytes, handle)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv")
     return out, lse
 
 

@@ -59,8 +59,103 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
   // keeps -inf (masked) scores at -inf after scaling; the floor changes no finite result.
   args->sl2 = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
   args->neg = scale < 0.0f ? 1 : 0;
+  args->kv_chunk = N;
+  args->part_u = nullptr;
+  args->part_ml = nullptr;
   *d_pad = dp;
   return FA_OK;
+}
+
+constexpr int kMaxSplits = 64;
+
+// Plan of a split-KV call: the number of split columns actually used, the keys per column and
+// the workspace bytes they need (0 when one column remains, i.e. the single-pass kernels run).
+struct SplitPlan {
+  int nsplit;
+  int kv_chunk;
+  int d_pad;
+  size_t u_bytes;    // partial numerators: nsplit * B*H * N * d_pad fp32
+  size_t ws_bytes;   // u_bytes rounded up to 256, plus the (m, l) pairs
+};
+
+int plan_split(int B, int H, int N, int d, int dtype, int causal, int num_splits, SplitPlan* p) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  if (d > 256) return FA_ERR_UNSUPPORTED;
+  const int dp = d <= 64 ? 64 : (d <= 128 ? 128 : 256);
+  const int tile = dtype == FA_BF16 ? fa::bf16_split_key_tile(dp) : fa::f32_split_key_tile(dp);
+  const int rows = dtype == FA_BF16 ? fa::bf16_split_rows_per_block(dp) : fa::f32_rows_per_block(dp);
+  const int64_t tiles = ((int64_t)N + tile - 1) / tile;
+  const int64_t base = (int64_t)B * H * (((int64_t)N + rows - 1) / rows);   // workgroups of one column
+  int64_t want = num_splits;
+  if (want == 0) {
+    // Library choice: enough columns for about one workgroup per CU of the 256, never more
+    // columns than key tiles.
+    want = base >= 256 ? 1 : (256 + base - 1) / base;
+  }
+  want = want < 1 ? 1 : (want > kMaxSplits ? kMaxSplits : want);
+  if (want > tiles) want = tiles;
+  const int64_t per = (tiles + want - 1) / want;              // tiles per column
+  const int64_t chunk = per * tile;
+  const int64_t ns = ((int64_t)N + chunk - 1) / chunk;        // no column without keys
+  p->nsplit = (int)ns;
+  p->kv_chunk = (int)(ns == 1 ? N : chunk);
+  p->d_pad = dp;
+  if (ns == 1) {
+    p->u_bytes = 0;
+    p->ws_bytes = 0;
+    return FA_OK;
+  }
+  const unsigned __int128 rows_all = (unsigned __int128)ns * B * H * N;
+  const unsigned __int128 ub = rows_all * dp * sizeof(float);
+  const unsigned __int128 total = ((ub + 255) / 256) * 256 + rows_all * 2 * sizeof(float);
+  if (total > ((unsigned __int128)1 << 62)) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * (((int64_t)N + rows - 1) / rows) > INT_MAX) return FA_ERR_UNSUPPORTED;
+  p->u_bytes = (size_t)ub;
+  p->ws_bytes = (size_t)total;
+  return FA_OK;
+}
+
+// Host checks of a split-KV call (before any HIP call): the plan and the arguments of the
+// single-pass call of that dtype. Fills `args` for the partial pass.
+int check_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                  float scale, int causal, int dtype, int num_splits, SplitPlan* plan, fa::FwdArgs* args) {
+  const int st = plan_split(B, H, N, d, dtype, causal, num_splits, plan);
+  if (st != FA_OK) return st;
+  int d_pad = 0;
+  const bool bf = dtype == FA_BF16;
+  return validate(q, k, v, o, lse, B, H, N, d, scale, causal, bf ? 2 : 4,
+                  bf ? fa::bf16_split_rows_per_block : fa::f32_rows_per_block, args, &d_pad);
+}
+
+// The split-KV call once the checks have passed and the workspace is known: partial pass over
+// (query tile, key column), then the merge. With one column it is the single-pass call.
+int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                float scale, int causal, int dtype, const SplitPlan& plan, fa::FwdArgs args, void* ws,
+                hipStream_t stream) {
+  const bool bf = dtype == FA_BF16;
+  if (plan.nsplit == 1) {
+    return bf ? fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+              : fa_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)o, lse, B, H, N, d, scale,
+                           causal, stream);
+  }
+  const int d_pad = plan.d_pad;
+  args.kv_chunk = plan.kv_chunk;
+  args.part_u = (float*)ws;
+  args.part_ml = (float*)((uint8_t*)ws + ((plan.u_bytes + 255) / 256) * 256);
+  const hipError_t e1 = bf ? fa::launch_bf16_partial(args, d_pad, causal != 0, plan.nsplit, stream)
+                           : fa::launch_f32_partial(args, d_pad, causal != 0, plan.nsplit, stream);
+  if (e1 != hipSuccess) return FA_ERR_HIP;
+  const hipError_t e2 = fa::launch_merge(args, d_pad, causal != 0, plan.nsplit, /*m_unscaled=*/!bf,
+                                         /*out_f32=*/!bf, stream);
+  return e2 == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+bool ranges_overlap(const void* x, uint64_t nx, const void* y, uint64_t ny) {
+  const uintptr_t a0 = (uintptr_t)x, b0 = (uintptr_t)y;
+  return a0 < b0 + ny && b0 < a0 + nx;
 }
 
 }  // namespace
@@ -83,6 +178,37 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
                           fa::f32_rows_per_block, &args, &d_pad);
   if (st != FA_OK) return st;
   return fa::launch_f32(args, d_pad, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_fwd_splitkv_plan(int B, int H, int N, int d, int dtype, int causal, int num_splits,
+                                   int* nsplit_out, size_t* workspace_bytes_out) {
+  SplitPlan plan;
+  const int st = plan_split(B, H, N, d, dtype, causal, num_splits, &plan);
+  if (st != FA_OK) return st;
+  if (nsplit_out != nullptr) *nsplit_out = plan.nsplit;
+  if (workspace_bytes_out != nullptr) *workspace_bytes_out = plan.ws_bytes;
+  return FA_OK;
+}
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int N, int d, float scale, int causal, int dtype, int num_splits,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  SplitPlan plan;
+  fa::FwdArgs args;
+  const int st = check_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, &plan, &args);
+  if (st != FA_OK) return st;
+  if (plan.nsplit > 1) {
+    if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return FA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return FA_ERR_INVALID_ARG;
+    // the workspace may not overlap any input or output
+    const size_t elem = dtype == FA_BF16 ? 2 : 4;
+    const uint64_t tb = (uint64_t)B * H * N * d * elem, lb = (uint64_t)B * H * N * sizeof(float);
+    const void* bufs[4] = {q, k, v, o};
+    for (const void* b : bufs)
+      if (b != nullptr && ranges_overlap(workspace, plan.ws_bytes, b, tb)) return FA_ERR_INVALID_ARG;
+    if (lse != nullptr && ranges_overlap(workspace, plan.ws_bytes, lse, lb)) return FA_ERR_INVALID_ARG;
+  }
+  return run_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, plan, args, workspace, stream);
 }
 
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -142,6 +268,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported problem (head dimension above 256 or problem too large)";
     case FA_ERR_HIP: return "HIP launch error";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_fwd_splitkv_plan reports";
     default: return "unknown status";
   }
 }

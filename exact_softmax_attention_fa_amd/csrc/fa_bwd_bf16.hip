@@ -608,6 +608,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const unsigned nblk = (unsigned)((a.N + NW * BLK - 1) / (NW * BLK));
   // dQ first: it writes delta, which the dK/dV kernel reads
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(NT), 0, stream, a);
+  // the dK/dV kernel reads the delta rows the dQ kernel writes: launch it only if that launch went in
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)a.BH * nblk), dim3(DKDV_NT), 0, stream, a);
   return hipGetLastError();
 }

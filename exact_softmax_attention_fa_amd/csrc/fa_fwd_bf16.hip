@@ -264,7 +264,9 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
 // may use the whole register file (larger ones keep the configured occupancy).
 template <int D, int SPLIT> constexpr int min_waves_per_simd() { return Cfg<D>::NW * SPLIT <= 2 ? 1 : Cfg<D>::WPE; }
 
-template <int D, bool CAUSAL, bool FULLD, int SPLIT>
+// PARTIAL: the workgroup covers only the keys of its split column (blockIdx.y) and writes its
+// partial state (m, l, u) to the workspace instead of o and lse; a merge pass combines them.
+template <int D, bool CAUSAL, bool FULLD, int SPLIT, bool PARTIAL>
 __global__ __launch_bounds__(Cfg<D>::NW * SPLIT * 64, (min_waves_per_simd<D, SPLIT>()))
 void fwd_bf16_kernel(FwdArgs a) {
   constexpr int QW = Cfg<D>::QW, NW = Cfg<D>::NW, BC = Cfg<D>::BC;
@@ -327,8 +329,18 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
+  // Key range of this workgroup: all keys up to the last query (causal) or N, restricted to
+  // its split column when the key range is split over workgroups. A column that holds no key
+  // any of its queries may see has nothing to contribute (the merge skips it).
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-  const int nkv = (kv_end + BC - 1) / BC;
+  int key_beg = 0, key_stop = kv_end;
+  if constexpr (PARTIAL) {
+    key_beg = (int)blockIdx.y * a.kv_chunk;
+    key_stop = min(kv_end, key_beg + a.kv_chunk);
+    if (key_beg >= key_stop) return;   // uniform over the workgroup, before any barrier
+  }
+  const int t_beg = key_beg / BC;                       // first tile (kv_chunk is a tile multiple)
+  const int nkv = (key_stop + BC - 1) / BC - t_beg;     // tiles of this workgroup
 
   f32x16 acc[QW][D / 32];
 #pragma unroll
@@ -346,7 +358,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   u32x4 kreg[CPT], vreg[CPT];
   // step `it` stages tiles it*SPLIT .. it*SPLIT + SPLIT-1 (one per key group)
   auto gload = [&](int it) {
-    const int key_lo = it * SPLIT * BC;
+    const int key_lo = (t_beg + it * SPLIT) * BC;
     const bool whole = FULLD && key_lo + SPLIT * BC <= N;   // no bounds checks needed
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
@@ -398,15 +410,19 @@ void fwd_bf16_kernel(FwdArgs a) {
   // diagonal, or the ragged last tile) take the masked path, and under a causal mask a wave
   // skips the tiles that lie entirely past its own last query. Key group g handles tiles
   // it*SPLIT + g.
-  const int j_split = CAUSAL ? min(N / BC, (q0 + 1) / BC) : N / BC;
-  const int it_split = j_split / SPLIT;   // steps whose tiles are all unmasked
+  // (tile indices below are relative to t_beg; in a split column the unmasked tiles end at the
+  // column's end or earlier, and may not exist at all)
+  const int j_unmasked = CAUSAL ? min(N / BC, (q0 + 1) / BC) : N / BC;
+  const int j_split = PARTIAL ? min(nkv, j_unmasked - t_beg) : j_unmasked;
+  const int it_split = PARTIAL ? max(j_split, 0) / SPLIT : j_split / SPLIT;   // steps whose tiles are all unmasked
   int it = 0;
   for (; it < it_split; ++it) {
     const int buf = it & 1;
     if (it + 1 < nit) gload(it + 1);
     const uint16_t* Ks = tile_buf(buf);
-    tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, (it * SPLIT + grpk) * BC, N,
-                                               wq_lo, a.sl2, lr, hh, tr_row, tr_col);
+    tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run,
+                                               (t_beg + it * SPLIT + grpk) * BC, N, wq_lo, a.sl2, lr, hh,
+                                               tr_row, tr_col);
     if (it + 1 < nit) swrite(buf ^ 1);
     __syncthreads();
   }
@@ -415,11 +431,12 @@ void fwd_bf16_kernel(FwdArgs a) {
     if (it + 1 < nit) gload(it + 1);
     const uint16_t* Ks = tile_buf(buf);
     const int t = it * SPLIT + grpk;
+    const int key0 = (t_beg + t) * BC;
     if (t < j_split)
-      tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, t * BC, N, wq_lo, a.sl2,
+      tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, key0, N, wq_lo, a.sl2,
                                                  lr, hh, tr_row, tr_col);
-    else if (t < nkv && (!CAUSAL || t * BC <= wq_hi))
-      tile_step<D, QW, BC, KP, VP, true, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, t * BC, N, wq_lo, a.sl2,
+    else if (t < nkv && (!CAUSAL || key0 <= wq_hi))
+      tile_step<D, QW, BC, KP, VP, true, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, key0, N, wq_lo, a.sl2,
                                                 lr, hh, tr_row, tr_col);
     if (it + 1 < nit) swrite(buf ^ 1);
     __syncthreads();
@@ -468,6 +485,32 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
+  // ---- partial epilogue: the state (m, l, u) of this key range, unnormalised ---------------
+  // m is the reference of the exponentials in base-2 units (-inf for a row that saw no key
+  // of this range; then l = 0 and u = 0).
+  if constexpr (PARTIAL) {
+    const size_t col_base = (size_t)blockIdx.y * a.BH + bh;
+#pragma unroll
+    for (int qb = 0; qb < QW; ++qb) {
+      const int qi = wq_lo + qb * 32 + lr;
+      const float l_tot = pair_sum(l_run[qb]);
+      if (qi < N) {
+        const size_t row = col_base * N + qi;
+        float* urow = a.part_u + row * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 w = {acc[qb][dt][4 * g + 0], acc[qb][dt][4 * g + 1], acc[qb][dt][4 * g + 2],
+                              acc[qb][dt][4 * g + 3]};
+            *(float4*)(urow + dt * 32 + 8 * g + 4 * hh) = w;
+          }
+        if (hh == 0) *(float2*)(a.part_ml + 2 * row) = make_float2(m_run[qb], l_tot);
+      }
+    }
+    return;
+  }
+
   // ---- epilogue: o = u / l, lse = (m + log2 l) * ln 2 ----------------------------------------
 #pragma unroll
   for (int qb = 0; qb < QW; ++qb) {
@@ -501,34 +544,48 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, int SPLIT>
-hipError_t launch_split(const FwdArgs& a, bool fulld, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.BH * a.n_qtiles));
+template <int D, bool CAUSAL, int SPLIT, bool PARTIAL>
+hipError_t launch_split(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.BH * a.n_qtiles), (unsigned)ncol);
   const dim3 block(Cfg<D>::NW * SPLIT * 64);
-  if (fulld) hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, SPLIT>), grid, block, 0, stream, a);
-  else       hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, SPLIT>), grid, block, 0, stream, a);
+  if (fulld) hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, SPLIT, PARTIAL>), grid, block, 0, stream, a);
+  else       hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, SPLIT, PARTIAL>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 // Key groups per workgroup: split the key range as far as MAXSPLIT allows when the grid has
 // at most one workgroup per CU, as long as every group still gets at least two tiles.
+// `keys` is the length of one workgroup's key range, `ncol` the number of split columns.
 template <int D>
-int choose_split(const FwdArgs& a) {
-  const long long wgs = (long long)a.BH * a.n_qtiles;
-  const int nkv = (a.N + Cfg<D>::BC - 1) / Cfg<D>::BC;
+int choose_split(const FwdArgs& a, int keys, int ncol) {
+  const long long wgs = (long long)a.BH * a.n_qtiles * ncol;
+  const int nkv = (keys + Cfg<D>::BC - 1) / Cfg<D>::BC;
   int split = 1;
   while (split * 2 <= Cfg<D>::MAXSPLIT && wgs <= FA_SPLIT_MAX_WGS && nkv >= 2 * split * 2) split *= 2;
   return split;
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
+template <int D, bool CAUSAL, bool PARTIAL>
+hipError_t launch_one(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
   if constexpr (Cfg<D>::MAXSPLIT >= 4) {
-    const int split = choose_split<D>(a);
-    if (split == 4) return launch_split<D, CAUSAL, 4>(a, fulld, stream);
-    if (split == 2) return launch_split<D, CAUSAL, 2>(a, fulld, stream);
+    const int split = choose_split<D>(a, PARTIAL ? a.kv_chunk : a.N, ncol);
+    if (split == 4) return launch_split<D, CAUSAL, 4, PARTIAL>(a, fulld, ncol, stream);
+    if (split == 2) return launch_split<D, CAUSAL, 2, PARTIAL>(a, fulld, ncol, stream);
   }
-  return launch_split<D, CAUSAL, 1>(a, fulld, stream);
+  return launch_split<D, CAUSAL, 1, PARTIAL>(a, fulld, ncol, stream);
+}
+
+template <bool PARTIAL>
+hipError_t launch_generic(const FwdArgs& a, int d_pad, bool causal, int ncol, hipStream_t stream) {
+  const bool fulld = (a.d == d_pad);
+  if (d_pad == 64)
+    return causal ? launch_one<64, true, PARTIAL>(a, fulld, ncol, stream)
+                  : launch_one<64, false, PARTIAL>(a, fulld, ncol, stream);
+  if (d_pad == 128)
+    return causal ? launch_one<128, true, PARTIAL>(a, fulld, ncol, stream)
+                  : launch_one<128, false, PARTIAL>(a, fulld, ncol, stream);
+  return causal ? launch_one<256, true, PARTIAL>(a, fulld, ncol, stream)
+                : launch_one<256, false, PARTIAL>(a, fulld, ncol, stream);
 }
 
 }  // namespace
@@ -542,10 +599,20 @@ int bf16_rows_per_block(int d) {
 
 hipError_t launch_bf16(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream) {
   if (a.d == 128) return launch_bf16_d128(a, causal, stream);
-  const bool fulld = (a.d == d_pad);
-  if (d_pad == 64) return causal ? launch_one<64, true>(a, fulld, stream) : launch_one<64, false>(a, fulld, stream);
-  if (d_pad == 128) return causal ? launch_one<128, true>(a, fulld, stream) : launch_one<128, false>(a, fulld, stream);
-  return causal ? launch_one<256, true>(a, fulld, stream) : launch_one<256, false>(a, fulld, stream);
+  return launch_generic<false>(a, d_pad, causal, 1, stream);
+}
+
+int bf16_split_rows_per_block(int d_pad) {
+  return d_pad <= 64 ? Cfg<64>::NW * Cfg<64>::QW * 32
+                     : (d_pad <= 128 ? Cfg<128>::NW * Cfg<128>::QW * 32 : Cfg<256>::NW * Cfg<256>::QW * 32);
+}
+
+int bf16_split_key_tile(int d_pad) {
+  return d_pad <= 64 ? Cfg<64>::BC : (d_pad <= 128 ? Cfg<128>::BC : Cfg<256>::BC);
+}
+
+hipError_t launch_bf16_partial(const FwdArgs& a, int d_pad, bool causal, int nsplit, hipStream_t stream) {
+  return launch_generic<true>(a, d_pad, causal, nsplit, stream);
 }
 
 }  // namespace fa

@@ -58,7 +58,9 @@ __device__ __forceinline__ f32x4 load4_masked(const float* row, int col, int d) 
   return r;
 }
 
-template <int D, bool CAUSAL, bool FULLD, int SPLIT>
+// PARTIAL: the workgroup covers only the keys of its split column (blockIdx.y) and writes its
+// partial state (m, l, u) to the workspace instead of o and lse; a merge pass combines them.
+template <int D, bool CAUSAL, bool FULLD, int SPLIT, bool PARTIAL>
 __global__ __launch_bounds__(CfgF<D>::NW * SPLIT * 64, 1)
 void fwd_f32_kernel(FwdArgs a) {
   constexpr int NW = CfgF<D>::NW, BC = CfgF<D>::BC;
@@ -126,8 +128,18 @@ void fwd_f32_kernel(FwdArgs a) {
     }
   }
 
+  // Key range of this workgroup: all keys up to the last query (causal) or N, restricted to
+  // its split column when the key range is split over workgroups. A column that holds no key
+  // any of its queries may see has nothing to contribute (the merge skips it).
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-  const int nkv = (kv_end + BC - 1) / BC;
+  int key_beg = 0, key_stop = kv_end;
+  if constexpr (PARTIAL) {
+    key_beg = (int)blockIdx.y * a.kv_chunk;
+    key_stop = min(kv_end, key_beg + a.kv_chunk);
+    if (key_beg >= key_stop) return;   // uniform over the workgroup, before any barrier
+  }
+  const int t_beg = key_beg / BC;                       // first tile (kv_chunk is a tile multiple)
+  const int nkv = (key_stop + BC - 1) / BC - t_beg;     // tiles of this workgroup
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -139,7 +151,7 @@ void fwd_f32_kernel(FwdArgs a) {
   f32x4 kreg[CPT], vreg[CPT];
   // step `it` stages tiles it*SPLIT .. it*SPLIT + SPLIT-1 (one per key group)
   auto gload = [&](int it) {
-    const int key0 = it * SPLIT * BC;
+    const int key0 = (t_beg + it * SPLIT) * BC;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + r * NT;
@@ -185,8 +197,8 @@ void fwd_f32_kernel(FwdArgs a) {
     if (it + 1 < nit) gload(it + 1);
     const float* Ks = smem + (buf * SPLIT + grpk) * (KT + VT);
     const float* Vs = Ks + KT;
-    const int j = it * SPLIT + grpk;   // this key group's tile
-    const int key0 = j * BC;
+    const int j = it * SPLIT + grpk;   // this key group's tile (relative to t_beg)
+    const int key0 = (t_beg + j) * BC;
 
     if (j < nkv && (!CAUSAL || key0 <= wq_hi)) {
       f32x16 s[BC / 32];
@@ -320,6 +332,26 @@ void fwd_f32_kernel(FwdArgs a) {
   }
 
   const float l_tot = pair_sum(l_run);
+
+  // ---- partial epilogue: the state (m, l, u) of this key range, unnormalised ---------------
+  // m is the running maximum of the unscaled scores (-inf for a row that saw no key of this
+  // range; then l = 0 and u = 0).
+  if constexpr (PARTIAL) {
+    if (qi < N) {
+      const size_t row = ((size_t)blockIdx.y * a.BH + bh) * N + qi;
+      float* urow = a.part_u + row * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 w = {acc[dt][4 * g + 0], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]};
+          *(float4*)(urow + dt * 32 + 8 * g + 4 * hh) = w;
+        }
+      if (hh == 0) *(float2*)(a.part_ml + 2 * row) = make_float2(m_run, l_tot);
+    }
+    return;
+  }
+
   const float inv = 1.0f / l_tot;
   if (qi < N) {
     float* orow = Oh + (size_t)qi * d;
@@ -346,30 +378,44 @@ void fwd_f32_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, int SPLIT>
-hipError_t launch_split(const FwdArgs& a, bool fulld, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.BH * a.n_qtiles));
+template <int D, bool CAUSAL, int SPLIT, bool PARTIAL>
+hipError_t launch_split(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.BH * a.n_qtiles), (unsigned)ncol);
   const dim3 block(CfgF<D>::NW * SPLIT * 64);
-  if (fulld) hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, true, SPLIT>), grid, block, 0, stream, a);
-  else       hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, false, SPLIT>), grid, block, 0, stream, a);
+  if (fulld) hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, true, SPLIT, PARTIAL>), grid, block, 0, stream, a);
+  else       hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, false, SPLIT, PARTIAL>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 // Key groups per workgroup: split the key range while the grid stays small (at most 512
-// workgroups) and every group still gets at least two tiles.
-template <int D, bool CAUSAL>
-hipError_t launch_one(const FwdArgs& a, bool fulld, hipStream_t stream) {
-  const long long wgs = (long long)a.BH * a.n_qtiles;
-  const int nkv = (a.N + CfgF<D>::BC - 1) / CfgF<D>::BC;
+// workgroups) and every group still gets at least two tiles. `keys` is the length of one
+// workgroup's key range, `ncol` the number of split columns.
+template <int D, bool CAUSAL, bool PARTIAL>
+hipError_t launch_one(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
+  const long long wgs = (long long)a.BH * a.n_qtiles * ncol;
+  const int nkv = ((PARTIAL ? a.kv_chunk : a.N) + CfgF<D>::BC - 1) / CfgF<D>::BC;
   int split = 1;
   while (split * 2 <= CfgF<D>::MAXSPLIT && wgs * split * 2 <= 512 && nkv >= 2 * split * 2) split *= 2;
   if constexpr (CfgF<D>::MAXSPLIT >= 4) {
-    if (split == 4) return launch_split<D, CAUSAL, 4>(a, fulld, stream);
+    if (split == 4) return launch_split<D, CAUSAL, 4, PARTIAL>(a, fulld, ncol, stream);
   }
   if constexpr (CfgF<D>::MAXSPLIT >= 2) {
-    if (split == 2) return launch_split<D, CAUSAL, 2>(a, fulld, stream);
+    if (split == 2) return launch_split<D, CAUSAL, 2, PARTIAL>(a, fulld, ncol, stream);
   }
-  return launch_split<D, CAUSAL, 1>(a, fulld, stream);
+  return launch_split<D, CAUSAL, 1, PARTIAL>(a, fulld, ncol, stream);
+}
+
+template <bool PARTIAL>
+hipError_t launch_generic(const FwdArgs& a, int d_pad, bool causal, int ncol, hipStream_t stream) {
+  const bool fulld = (a.d == d_pad);
+  if (d_pad == 64)
+    return causal ? launch_one<64, true, PARTIAL>(a, fulld, ncol, stream)
+                  : launch_one<64, false, PARTIAL>(a, fulld, ncol, stream);
+  if (d_pad == 128)
+    return causal ? launch_one<128, true, PARTIAL>(a, fulld, ncol, stream)
+                  : launch_one<128, false, PARTIAL>(a, fulld, ncol, stream);
+  return causal ? launch_one<256, true, PARTIAL>(a, fulld, ncol, stream)
+                : launch_one<256, false, PARTIAL>(a, fulld, ncol, stream);
 }
 
 }  // namespace
@@ -379,10 +425,15 @@ int f32_rows_per_block(int d) {
 }
 
 hipError_t launch_f32(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream) {
-  const bool fulld = (a.d == d_pad);
-  if (d_pad == 64) return causal ? launch_one<64, true>(a, fulld, stream) : launch_one<64, false>(a, fulld, stream);
-  if (d_pad == 128) return causal ? launch_one<128, true>(a, fulld, stream) : launch_one<128, false>(a, fulld, stream);
-  return causal ? launch_one<256, true>(a, fulld, stream) : launch_one<256, false>(a, fulld, stream);
+  return launch_generic<false>(a, d_pad, causal, 1, stream);
+}
+
+int f32_split_key_tile(int d_pad) {
+  return d_pad <= 64 ? CfgF<64>::BC : (d_pad <= 128 ? CfgF<128>::BC : CfgF<256>::BC);
+}
+
+hipError_t launch_f32_partial(const FwdArgs& a, int d_pad, bool causal, int nsplit, hipStream_t stream) {
+  return launch_generic<true>(a, d_pad, causal, nsplit, stream);
 }
 
 }  // namespace fa

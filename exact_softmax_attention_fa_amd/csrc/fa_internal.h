@@ -1,6 +1,7 @@
 // Internal launch interface between the C-ABI front end (fa_api.hip) and the kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace fa {
@@ -19,6 +20,15 @@ struct FwdArgs {
   int n_qtiles;   // ceil(N / rows per workgroup)
   float sl2;      // |scale| * log2(e): scores are kept in base-2 exponent units
   int neg;        // 1 when scale < 0: the kernel negates q (exact) and uses |scale|
+  // Key-range split over workgroups (generic kernels only). Workgroup column y = blockIdx.y
+  // takes keys [y * kv_chunk, (y + 1) * kv_chunk); kv_chunk is a multiple of the kernel's key
+  // tile. With part_u == nullptr there is one column (kv_chunk >= N) and the kernel writes o
+  // and lse; otherwise it writes its partial state (m, l, u) instead:
+  //   part_u  [split][BH][N][d_pad] fp32: unnormalised numerator u
+  //   part_ml [split][BH][N][2]     fp32: reference m (see part_m_unscaled) and denominator l
+  int kv_chunk;
+  float* part_u;
+  float* part_ml;
 };
 
 // Rows of queries per workgroup of the kernel that will run for head width d (host needs it
@@ -26,7 +36,7 @@ struct FwdArgs {
 int bf16_rows_per_block(int d);
 int f32_rows_per_block(int d);
 
-// Enqueue one forward pass. d_pad (64 or 128) is the padded head width of the generic
+// Enqueue one forward pass. d_pad (64, 128 or 256) is the padded head width of the generic
 // kernels. Return hipSuccess or the launch error.
 hipError_t launch_bf16(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream);
 hipError_t launch_f32(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream);
@@ -34,5 +44,23 @@ hipError_t launch_f32(const FwdArgs& a, int d_pad, bool causal, hipStream_t stre
 // Tuned bf16 kernel for head width exactly 128 (rows per workgroup, launch).
 int bf16_d128_rows_per_block();
 hipError_t launch_bf16_d128(const FwdArgs& a, bool causal, hipStream_t stream);
+
+// ---- key-range split (split-KV) -------------------------------------------------------------
+// Rows per workgroup and keys per tile of the generic kernel that runs the partial pass
+// (split path: the generic kernels serve every width, d = 128 included).
+int bf16_split_rows_per_block(int d_pad);
+int bf16_split_key_tile(int d_pad);
+int f32_split_key_tile(int d_pad);
+// Partial pass: grid (BH * n_qtiles, nsplit); every workgroup writes part_u / part_ml for its
+// rows and keys (workgroups whose key range lies past their last query under the causal mask
+// write nothing; the merge never reads those entries).
+hipError_t launch_bf16_partial(const FwdArgs& a, int d_pad, bool causal, int nsplit, hipStream_t stream);
+hipError_t launch_f32_partial(const FwdArgs& a, int d_pad, bool causal, int nsplit, hipStream_t stream);
+// Merge pass: o and lse from the nsplit partial states of every row. m_unscaled = 1 when the
+// partial kernels keep m on unscaled scores (fp32 kernel: weights 2^((m_s - m*) * sl2)),
+// 0 when m is already in base-2 units (bf16 kernel: weights 2^(m_s - m*)). out_f32 selects
+// the output type (fp32 or bf16).
+hipError_t launch_merge(const FwdArgs& a, int d_pad, bool causal, int nsplit, bool m_unscaled, bool out_f32,
+                        hipStream_t stream);
 
 }  // namespace fa

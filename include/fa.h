@@ -38,6 +38,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -49,8 +50,13 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null q/k/v/o, B/H/N/d < 1, non-finite or non-positive-size problem,
                               causal not 0/1, element count above 2^62 */
   FA_ERR_UNSUPPORTED = -2, /* d > 256 (the largest head width compiled), or a grid too large */
-  FA_ERR_HIP = -3          /* the HIP runtime rejected the launch */
+  FA_ERR_HIP = -3,         /* the HIP runtime rejected the launch */
+  FA_ERR_WORKSPACE = -4    /* split-KV call: workspace missing or smaller than required */
 } fa_status;
+
+/* Element type selector of the split-KV entry points (the single-pass entry points carry the
+ * type in their names instead). */
+typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
 
 /* bf16 inputs and output (the hot path).
  *   q, k, v : device, bf16 (IEEE binary32 upper halves), [B][H][N][d], read only
@@ -87,6 +93,43 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, float* delta,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Forward pass with the key range split over several workgroups (split-KV), for grids that
+ * the single-pass kernels leave small: few heads, few query tiles, long key ranges.
+ *
+ * Every query tile is paired with each of S consecutive key ranges ("split columns"); each
+ * pair runs as its own workgroup and leaves the partial online-softmax state of its rows in
+ * the workspace: the reference maximum m_s, the denominator l_s and the unnormalised numerator
+ * u_s. A second kernel merges the S states of every row with the rule for combining two blocks
+ * (interactiveml.org, "FlashAttention saves the matrix, not the quadratic work", merge of the
+ * three sufficient statistics): m* = max m_s, l = sum e^(m_s - m*) l_s, u = sum e^(m_s - m*) u_s,
+ * o = u / l, lse = m* + ln l. The result is the function fa_fwd / fa_fwd_f32 computes (same
+ * arguments, same layouts and outputs), up to rounding.
+ *   dtype      : FA_BF16 (q, k, v, o bf16, as fa_fwd) or FA_F32 (fp32, as fa_fwd_f32)
+ *   num_splits : 0 = the library's choice (about one workgroup per CU), else 1..64 requested
+ *                columns; the call uses at most one column per key tile of the kernel and
+ *                drops columns that would hold no key (fa_fwd_splitkv_plan reports the count)
+ *   workspace  : device memory owned by the caller, 256-byte aligned, at least the size
+ *                fa_fwd_splitkv_plan reports for the same (B, H, N, d, dtype, causal,
+ *                num_splits); its contents on entry are ignored and on return unspecified.
+ *                It must not overlap q, k, v, o or lse. When the plan has one column
+ *                (workspace size 0) the call is the single-pass fa_fwd / fa_fwd_f32 and the
+ *                workspace may be NULL.
+ * The library allocates nothing. Two kernels are enqueued on `stream` (partial pass, merge);
+ * calls that share a workspace must be ordered (same stream or synchronised). Errors as for
+ * fa_fwd, plus FA_ERR_WORKSPACE (missing or too small workspace) and FA_ERR_INVALID_ARG for
+ * dtype not in {FA_BF16, FA_F32}, num_splits outside 0..64 or a misaligned or overlapping
+ * workspace. */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal, int dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Host-only planning of a fa_fwd_splitkv call (no HIP call): writes the number of split
+ * columns the call will use and the workspace bytes it needs (0 when one column remains) to
+ * the non-NULL output pointers. Returns FA_OK or the status fa_fwd_splitkv would return for
+ * these sizes (FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED). */
+int fa_fwd_splitkv_plan(int B, int H, int N, int d, int dtype, int causal, int num_splits,
+                        int* nsplit_out, size_t* workspace_bytes_out);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);

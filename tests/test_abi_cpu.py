@@ -28,7 +28,8 @@ def lib():
 
 
 def test_header_declares_entry_points():
-    assert header_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_status_string"]
+    assert header_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_plan",
+                                  "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -45,6 +46,7 @@ def test_status_strings(lib):
     assert fa.fa_status_string(fa.FA_ERR_INVALID_ARG) == "invalid argument"
     assert "256" in fa.fa_status_string(fa.FA_ERR_UNSUPPORTED)
     assert fa.fa_status_string(fa.FA_ERR_HIP) == "HIP launch error"
+    assert "workspace" in fa.fa_status_string(fa.FA_ERR_WORKSPACE)
     assert fa.fa_status_string(12345) == "unknown status"
 
 
@@ -136,3 +138,96 @@ def test_oracle_imports_nothing_from_the_product():
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert "exact_softmax_attention_fa_amd" not in text, f
             assert "torch" not in text, f
+
+
+# ---- split-KV planning and host checks (no HIP call is made by any of these) ---------------
+
+def plan(B=1, H=1, N=256, d=64, dtype=fa.FA_F32, causal=0, num_splits=0):
+    return fa.fa_fwd_splitkv_plan(B, H, N, d, dtype, causal, num_splits)
+
+
+def expected_plan(B, H, N, d, dtype, num_splits, tile, rows):
+    """The plan rule restated: at most one column per key tile, columns of whole tiles, no
+    empty column; the default aims at about one workgroup per CU (256)."""
+    import math
+    dp = 64 if d <= 64 else (128 if d <= 128 else 256)
+    tiles = math.ceil(N / tile)
+    base = B * H * math.ceil(N / rows)
+    want = num_splits or (1 if base >= 256 else math.ceil(256 / base))
+    want = max(1, min(want, 64, tiles))
+    chunk = math.ceil(tiles / want) * tile
+    ns = math.ceil(N / chunk)
+    if ns == 1:
+        return 1, 0
+    rows_all = ns * B * H * N
+    u = rows_all * dp * 4
+    return ns, (u + 255) // 256 * 256 + rows_all * 8
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,ns", [
+    (1, 1, 256, 64, fa.FA_F32, 0),      # the fp32 single-head workload: 8 query tiles, 8 key tiles
+    (1, 1, 256, 64, fa.FA_F32, 3),
+    (1, 1, 256, 64, fa.FA_F32, 64),     # clamped to the 8 key tiles
+    (1, 1, 8192, 128, fa.FA_BF16, 0),
+    (1, 1, 8192, 128, fa.FA_BF16, 7),
+    (2, 8, 1024, 64, fa.FA_BF16, 0),    # 256 workgroups already: one column
+    (1, 2, 1000, 96, fa.FA_BF16, 5),
+    (1, 1, 33, 200, fa.FA_F32, 4),      # 2 key tiles of 32
+    (1, 1, 1, 64, fa.FA_BF16, 8),       # one key: one column
+])
+def test_splitkv_plan(lib, B, H, N, d, dtype, ns):
+    st, nsplit, wbytes = plan(B, H, N, d, dtype, 0, ns)
+    assert st == fa.FA_OK
+    if dtype == fa.FA_F32:
+        tile, rows = 32, {64: 32, 128: 64, 256: 128}[64 if d <= 64 else (128 if d <= 128 else 256)]
+    else:
+        tile = 32 if d > 128 else 64
+        rows = {64: 64, 128: 256, 256: 128}[64 if d <= 64 else (128 if d <= 128 else 256)]
+    assert (nsplit, wbytes) == expected_plan(B, H, N, d, dtype, ns, tile, rows)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(num_splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=65), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=2), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=257), fa.FA_ERR_UNSUPPORTED),
+])
+def test_splitkv_plan_rejects(lib, kwargs, status):
+    assert plan(**kwargs)[0] == status
+
+
+WS = 11 * BIG
+
+
+def call_split(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=256, d=64, scale=0.125, causal=0, dtype=fa.FA_F32,
+               num_splits=8, ws=WS, ws_bytes=1 << 30):
+    return fa.fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=100), fa.FA_ERR_INVALID_ARG),
+    (dict(d=300), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=1000), fa.FA_ERR_WORKSPACE),
+    (dict(ws=WS + 16), fa.FA_ERR_INVALID_ARG),          # not 256-byte aligned
+    (dict(ws=O + 256), fa.FA_ERR_INVALID_ARG),          # overlaps o
+    (dict(ws=L - 256), fa.FA_ERR_INVALID_ARG),          # overlaps lse
+    (dict(o=Q + 64), fa.FA_ERR_INVALID_ARG),            # o overlaps q
+])
+def test_splitkv_invalid_arguments_rejected_on_host(lib, kwargs, status):
+    assert call_split(**kwargs) == status
+
+
+def test_splitkv_workspace_exactly_the_plan_passes_host_checks(lib):
+    """A workspace of exactly the planned size passes the size check (one byte less does not);
+    checked with an invalid q so that nothing is launched."""
+    st, ns, need = plan(num_splits=8)
+    assert ns == 8 and need > 0
+    assert call_split(q=None, ws_bytes=need) == fa.FA_ERR_INVALID_ARG
+    assert call_split(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
