@@ -10,6 +10,8 @@ Entry points with the C names:
   fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, workspace,
                  workspace_bytes, stream)                      -> status   (key range split)
   fa_fwd_splitkv_plan(B, H, N, d, dtype, causal, num_splits)   -> (status, nsplit, workspace bytes)
+  fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, stream)
+                                                               -> status   (library-owned buffer)
   fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream) -> status
   fa_status_string(status)                                     -> str
 and tensor-level conveniences:
@@ -24,11 +26,13 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_plan", "fa_bwd", "fa_status_string",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_plan", "fa_fwd_splitkv_noalloc", "fa_bwd",
+           "fa_status_string", "FA_ERR_SCRATCH", "FA_NOALLOC_SCRATCH_BYTES",
            "fwd", "fwd_splitkv", "bwd", "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_BF16", "FA_F32", "FaError"]
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_WORKSPACE, FA_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 FA_BF16, FA_F32 = 0, 1
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +77,8 @@ def load_library():
     lib.fa_fwd_splitkv.argtypes = argtypes[:11] + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                                    ctypes.c_void_p]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = argtypes[:11] + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.fa_fwd_splitkv_plan.argtypes = [ctypes.c_int] * 7 + [ctypes.POINTER(ctypes.c_int),
                                                              ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_fwd_splitkv_plan.restype = ctypes.c_int
@@ -97,6 +103,12 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits
     """Split-KV forward on raw device pointers (ints); returns the C status code."""
     return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, workspace,
                                          workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, stream) -> int:
+    """Split-KV forward with the library's own partial-state buffer (allocates nothing)."""
+    return load_library().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits,
+                                                 stream)
 
 
 def fa_fwd_splitkv_plan(B, H, N, d, dtype, causal, num_splits):

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_bf16_d128.hip", "fa_fwd_f32.hip", "fa_splitkv.hip",
-           "fa_bwd_bf16.hip"]
+           "fa_noalloc.hip", "fa_bwd_bf16.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -68,15 +68,7 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
 
 constexpr int kMaxSplits = 64;
 
-// Plan of a split-KV call: the number of split columns actually used, the keys per column and
-// the workspace bytes they need (0 when one column remains, i.e. the single-pass kernels run).
-struct SplitPlan {
-  int nsplit;
-  int kv_chunk;
-  int d_pad;
-  size_t u_bytes;    // partial numerators: nsplit * B*H * N * d_pad fp32
-  size_t ws_bytes;   // u_bytes rounded up to 256, plus the (m, l) pairs
-};
+using fa::SplitPlan;
 
 int plan_split(int B, int H, int N, int d, int dtype, int causal, int num_splits, SplitPlan* p) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
@@ -118,9 +110,16 @@ int plan_split(int B, int H, int N, int d, int dtype, int causal, int num_splits
   return FA_OK;
 }
 
-// Host checks of a split-KV call (before any HIP call): the plan and the arguments of the
-// single-pass call of that dtype. Fills `args` for the partial pass.
-int check_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+bool ranges_overlap(const void* x, uint64_t nx, const void* y, uint64_t ny) {
+  const uintptr_t a0 = (uintptr_t)x, b0 = (uintptr_t)y;
+  return a0 < b0 + ny && b0 < a0 + nx;
+}
+
+}  // namespace
+
+namespace fa {
+
+int splitkv_check(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                   float scale, int causal, int dtype, int num_splits, SplitPlan* plan, fa::FwdArgs* args) {
   const int st = plan_split(B, H, N, d, dtype, causal, num_splits, plan);
   if (st != FA_OK) return st;
@@ -130,9 +129,7 @@ int check_splitkv(const void* q, const void* k, const void* v, void* o, float* l
                   bf ? fa::bf16_split_rows_per_block : fa::f32_rows_per_block, args, &d_pad);
 }
 
-// The split-KV call once the checks have passed and the workspace is known: partial pass over
-// (query tile, key column), then the merge. With one column it is the single-pass call.
-int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+int splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                 float scale, int causal, int dtype, const SplitPlan& plan, fa::FwdArgs args, void* ws,
                 hipStream_t stream) {
   const bool bf = dtype == FA_BF16;
@@ -153,12 +150,7 @@ int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse
   return e2 == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-bool ranges_overlap(const void* x, uint64_t nx, const void* y, uint64_t ny) {
-  const uintptr_t a0 = (uintptr_t)x, b0 = (uintptr_t)y;
-  return a0 < b0 + ny && b0 < a0 + nx;
-}
-
-}  // namespace
+}  // namespace fa
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
@@ -195,7 +187,7 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   SplitPlan plan;
   fa::FwdArgs args;
-  const int st = check_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, &plan, &args);
+  const int st = fa::splitkv_check(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_splits, &plan, &args);
   if (st != FA_OK) return st;
   if (plan.nsplit > 1) {
     if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return FA_ERR_WORKSPACE;
@@ -208,7 +200,7 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
       if (b != nullptr && ranges_overlap(workspace, plan.ws_bytes, b, tb)) return FA_ERR_INVALID_ARG;
     if (lse != nullptr && ranges_overlap(workspace, plan.ws_bytes, lse, lb)) return FA_ERR_INVALID_ARG;
   }
-  return run_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, plan, args, workspace, stream);
+  return fa::splitkv_run(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, plan, args, workspace, stream);
 }
 
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -269,6 +261,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported problem (head dimension above 256 or problem too large)";
     case FA_ERR_HIP: return "HIP launch error";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_fwd_splitkv_plan reports";
+    case FA_ERR_SCRATCH:
+      return "problem needs more partial-state memory than the fixed 64 MiB buffer of fa_fwd_splitkv_noalloc";
     default: return "unknown status";
   }
 }

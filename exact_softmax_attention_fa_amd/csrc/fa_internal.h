@@ -63,4 +63,25 @@ hipError_t launch_f32_partial(const FwdArgs& a, int d_pad, bool causal, int nspl
 hipError_t launch_merge(const FwdArgs& a, int d_pad, bool causal, int nsplit, bool m_unscaled, bool out_f32,
                         hipStream_t stream);
 
+// ---- split-KV front end (shared by the entry points with and without a caller workspace) ----
+// Plan of a split-KV call: the number of split columns actually used, the keys per column and
+// the workspace bytes they need (0 when one column remains, i.e. the single-pass kernels run).
+struct SplitPlan {
+  int nsplit;
+  int kv_chunk;
+  int d_pad;
+  size_t u_bytes;    // partial numerators: nsplit * B*H * N * d_pad fp32
+  size_t ws_bytes;   // u_bytes rounded up to 256, plus the (m, l) pairs
+};
+// Host checks of a split-KV call (before any HIP call): the plan and the arguments of the
+// single-pass call of that dtype. Fills `plan` and `args`; returns an fa_status code.
+int splitkv_check(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                  float scale, int causal, int dtype, int num_splits, SplitPlan* plan, FwdArgs* args);
+// The split-KV call once the checks have passed: partial pass over (query tile, key column)
+// into `ws` (plan.ws_bytes, 256-byte aligned), then the merge; with one column, the
+// single-pass call. Returns an fa_status code.
+int splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                float scale, int causal, int dtype, const SplitPlan& plan, FwdArgs args, void* ws,
+                hipStream_t stream);
+
 }  // namespace fa

@@ -51,7 +51,9 @@ typedef enum {
                               causal not 0/1, element count above 2^62 */
   FA_ERR_UNSUPPORTED = -2, /* d > 256 (the largest head width compiled), or a grid too large */
   FA_ERR_HIP = -3,         /* the HIP runtime rejected the launch */
-  FA_ERR_WORKSPACE = -4    /* split-KV call: workspace missing or smaller than required */
+  FA_ERR_WORKSPACE = -4,   /* split-KV call: workspace missing or smaller than required */
+  FA_ERR_SCRATCH = -5      /* fa_fwd_splitkv_noalloc: the partial states would not fit its
+                              fixed buffer of FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 /* Element type selector of the split-KV entry points (the single-pass entry points carry the
@@ -130,6 +132,23 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  * these sizes (FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED). */
 int fa_fwd_splitkv_plan(int B, int H, int N, int d, int dtype, int causal, int num_splits,
                         int* nsplit_out, size_t* workspace_bytes_out);
+
+/* Size of the device buffer fa_fwd_splitkv_noalloc keeps its partial states in (64 MiB per GPU,
+ * held from the library's first use on that GPU until the process ends). */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* fa_fwd_splitkv without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * partial states go to a fixed buffer the library owns, one per GPU (the GPU of `stream`, or
+ * the current GPU for the NULL stream). The call itself allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine. Arguments, result and errors as for fa_fwd_splitkv;
+ * a plan whose workspace (fa_fwd_splitkv_plan) exceeds FA_NOALLOC_SCRATCH_BYTES is rejected
+ * with FA_ERR_SCRATCH before any launch.
+ * All calls on one GPU share the buffer: calls that overlap on one GPU (different streams, or
+ * host threads without ordering) race and must be serialised by the caller. */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, int d, float scale, int causal, int dtype, int num_splits,
+                           hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -28,8 +28,8 @@ def lib():
 
 
 def test_header_declares_entry_points():
-    assert header_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_plan",
-                                  "fa_status_string"]
+    assert header_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc",
+                                  "fa_fwd_splitkv_plan", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -231,3 +231,17 @@ def test_splitkv_workspace_exactly_the_plan_passes_host_checks(lib):
     assert ns == 8 and need > 0
     assert call_split(q=None, ws_bytes=need) == fa.FA_ERR_INVALID_ARG
     assert call_split(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=5), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=65), fa.FA_ERR_INVALID_ARG),
+    (dict(d=300), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1, H=4, N=65536, d=128, dtype=fa.FA_BF16, num_splits=64), fa.FA_ERR_SCRATCH),   # > 64 MiB of states
+])
+def test_noalloc_rejects_on_host(lib, kwargs, status):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=256, d=64, scale=0.125, causal=0, dtype=fa.FA_F32, num_splits=8)
+    a.update(kwargs)
+    assert fa.fa_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                                     a["scale"], a["causal"], a["dtype"], a["num_splits"], None) == status
