@@ -293,7 +293,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.ALL_WORKLOADS))
     ap.add_argument("--settle-s", type=float, default=0.2,
                     help="untimed calls before the warm-up steps until the GPU has run this long "
                          "(the clock ramps up over the first tens of milliseconds)")
@@ -328,7 +328,7 @@ def main() -> int:
     import torch
     import exact_softmax_attention_fa_amd as fa
 
-    w = inputs.WORKLOADS[args.workload]
+    w = inputs.ALL_WORKLOADS[args.workload]
     t = inputs.make(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

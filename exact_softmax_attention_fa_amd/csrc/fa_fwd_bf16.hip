@@ -548,8 +548,15 @@ template <int D, bool CAUSAL, int SPLIT, bool PARTIAL>
 hipError_t launch_split(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
   const dim3 grid((unsigned)(a.BH * a.n_qtiles), (unsigned)ncol);
   const dim3 block(Cfg<D>::NW * SPLIT * 64);
-  if (fulld) hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, SPLIT, PARTIAL>), grid, block, 0, stream, a);
-  else       hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, SPLIT, PARTIAL>), grid, block, 0, stream, a);
+  // (head width exactly 128 runs on the tuned kernel in a single pass, so the generic 128-wide
+  // kernel is built for full rows only where the split pass uses it)
+  if constexpr (D != 128 || PARTIAL) {
+    if (fulld) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, SPLIT, PARTIAL>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, SPLIT, PARTIAL>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -97,6 +97,23 @@ WORKLOADS = {
 # Workload whose throughput is the headline figure.
 HEADLINE = "fwd_bf16_b1_h16_n8192_d128_widek"
 
+# Measurement-only shapes (not parity configurations of their own; the GPU tests cover their
+# kernels at smaller sizes): the head-width sweep at the headline's B, H, N with plain N(0,1)
+# inputs, and single heads of long sequences, where one query-tile column leaves most of the
+# chip idle and the key range is split over workgroups.
+EXTRA_WORKLOADS = {
+    **{f"sweep_bf16_b1_h16_n8192_d{d}": Workload(
+        f"sweep_bf16_b1_h16_n8192_d{d}", 1, 16, 8192, d, "bf16", False, 1100 + d,
+        note=f"head-width sweep: bf16 N(0,1) inputs, d = {d}, unmasked") for d in (32, 64, 96, 128, 256)},
+    "fwd_bf16_b1_h1_n8192_d128": Workload(
+        "fwd_bf16_b1_h1_n8192_d128", 1, 1, 8192, 128, "bf16", False, 1201,
+        note="one head of the headline shape, bf16 N(0,1) inputs, unmasked"),
+    "fwd_bf16_b1_h1_n32768_d128_causal": Workload(
+        "fwd_bf16_b1_h1_n32768_d128_causal", 1, 1, 32768, 128, "bf16", True, 1202,
+        note="one head of the long-context shape, bf16 N(0,1) inputs, causal"),
+}
+ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
+
 
 def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
     x32 = x64.astype(np.float32)
