@@ -75,7 +75,10 @@ int plan_split(int B, int H, int N, int d, int dtype, int causal, int num_splits
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  // the size limits of the single-pass calls, before any product of the sizes below
+  if ((unsigned __int128)B * H * N * d > ((unsigned __int128)1 << 62)) return FA_ERR_INVALID_ARG;
   if (d > 256) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)N * d > INT_MAX) return FA_ERR_UNSUPPORTED;
   const int dp = d <= 64 ? 64 : (d <= 128 ? 128 : 256);
   const int tile = dtype == FA_BF16 ? fa::bf16_split_key_tile(dp) : fa::f32_split_key_tile(dp);
   const int rows = dtype == FA_BF16 ? fa::bf16_split_rows_per_block(dp) : fa::f32_rows_per_block(dp);

@@ -31,6 +31,7 @@
 #include <math.h>
 
 #include "fa_bwd_internal.h"
+#include "fa_dma.h"
 
 namespace fa {
 namespace {
@@ -64,14 +65,9 @@ __device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32
 }
 
 // Staged [32][D] bf16 tiles sit in LDS without padding: 16-byte chunk L of row r is stored at
-// chunk position L ^ swz(r). With this permutation the 16 rows that one 16-lane quarter of a
-// 16-byte row read touches land in 16 different bank groups, and the 4 rows x 4 chunks that
-// each half of a transposed read touches do too, so neither access pattern conflicts.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  static_assert(D == 64 || D == 128, "head width");
-  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
+// chunk position L ^ swz(r) (fa_dma.h), which keeps both the row reads and the transposed reads
+// free of bank conflicts.
+using dma::swz;
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int chunk) { return r * D + 8 * (chunk ^ swz<D>(r)); }
 
@@ -207,9 +203,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int kb = (min(lw, NW - 1) * RPW + i) % KB_TILE;
-    const int r = kb * (512 / D) + lane / NC;
-    dma_row[i] = r;
-    dma_off[i] = (uint32_t)(r * 2 * D + 16 * ((lane % NC) ^ swz<D>(r)));
+    dma_row[i] = dma::tile_row<D>(kb, lane);
+    dma_off[i] = dma::tile_off<D>(kb, lane);
   }
   const float* stat_src = lw == 0 ? a.lse + (size_t)bh * N : a.delta + (size_t)bh * N;
   auto issue = [&](int qb, int slot) __attribute__((always_inline)) {
@@ -220,8 +215,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const uint8_t* src = tile_src + (size_t)row0 * 2 * D;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-      const int over = row0 + dma_row[i] - (N - 1);
-      const uint32_t back = over > 0 ? (uint32_t)over * 2u * D : 0u;
+      const uint32_t back = dma::past_end_back(row0, dma_row[i], N, 2 * D);
       const int kb = (lw * RPW + i) % KB_TILE;
       dma16(src, dma_off[i] - back, dst + (uint32_t)(kb * 1024));
     }
@@ -514,20 +508,19 @@ void bwd_dq_kernel(BwdArgs a) {
   uint32_t dma_off[KB_SUB];
 #pragma unroll
   for (int i = 0; i < KB_SUB; ++i) {
-    const int r = i * (512 / D) + lane / NC;
-    dma_row[i] = r;
-    dma_off[i] = (uint32_t)(r * 2 * D + 16 * ((lane % NC) ^ swz<D>(r)));
+    dma_row[i] = dma::tile_row<D>(i, lane);
+    dma_off[i] = dma::tile_off<D>(i, lane);
   }
   auto issue = [&](int t, int slot) __attribute__((always_inline)) {
     // first key of this wave's sub-tile, clamped so that every offset below is >= 0
-    const int row0 = min(2 * t * BLK + (wave & 1) * BLK, N - 1);
+    static_assert(BLK == 32, "sub-tiles of the load arithmetic");
+    const int row0 = dma::dq_row0(t, wave, N);
     const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(lds_base + (uint32_t)(slot * SLOT * 2 + wave * KT * 2)));
     const uint8_t* src = ld_src + (size_t)row0 * 2 * D;
 #pragma unroll
     for (int i = 0; i < KB_SUB; ++i) {
-      const int over = row0 + dma_row[i] - (N - 1);   // rows past N-1 read row N-1
-      const uint32_t back = over > 0 ? (uint32_t)over * 2u * D : 0u;
+      const uint32_t back = dma::past_end_back(row0, dma_row[i], N, 2 * D);   // rows past N-1 read row N-1
       dma16(src, dma_off[i] - back, dst + (uint32_t)(i * 1024));
     }
   };

@@ -44,6 +44,7 @@
 #include <math.h>
 
 #include "fa_internal.h"
+#include "fa_dma.h"
 
 namespace fa {
 namespace {
@@ -175,15 +176,14 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // of row (2*wave+i)*4 + l/16 and so fetches the logical chunk the swizzle places there.
   // The per-lane byte offsets inside a tile are fixed; the tile's base address advances in
   // scalar registers, so issuing a whole tile costs no vector instructions.
+  static_assert(dma::kFwd128RowBytes == ROWB, "row size of the load arithmetic");
   uint32_t gk_off[2], gv_off[2];
   int dma_row[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int row = (2 * wave + i) * 4 + (lane >> 4);
-    const int phys = lane & 15;
-    dma_row[i] = row;
-    gk_off[i] = (uint32_t)(row * ROWB + ((phys ^ (row & 15)) * 16));
-    gv_off[i] = (uint32_t)(row * ROWB + ((phys ^ ((row & 3) << 2)) * 16));
+    dma_row[i] = dma::fwd128_row(wave, lane, i);
+    gk_off[i] = dma::fwd128_k_off(wave, lane, i);
+    gv_off[i] = dma::fwd128_v_off(wave, lane, i);
   }
   // LDS byte address of the buffer (address-space cast, then the 32-bit LDS offset)
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
@@ -205,8 +205,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
     } else {   // ragged last tile: rows past the end read row N-1 instead (weight 0 later)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int over = key0 + dma_row[i] - (N - 1);
-        const uint32_t back = over > 0 ? (uint32_t)over * ROWB : 0u;
+        const uint32_t back = dma::past_end_back(key0, dma_row[i], N, ROWB);
         const uint32_t ldst = dma_lds + slot + (uint32_t)(i * 1024);
         dma16(kt, gk_off[i] - back, ldst);
         dma16(vt, gv_off[i] - back, ldst + VREGION);

@@ -1,0 +1,183 @@
+// Host-side walk of every global -> LDS tile load the kernels issue, for a list of sequence
+// lengths, with the address arithmetic the kernels use (fa_dma.h). For each 16-byte load it
+// checks that the global offset is non-negative and inside the head's N rows, that it reads the
+// row it should (rows past N-1 read row N-1) and the logical chunk the swizzle places at its LDS
+// position, that it writes inside its LDS slot, and that every 16-byte place of a tile is
+// written exactly once. The loop structure (which tiles each kernel issues for a given N and
+// mask) restates the kernels' own.
+//
+// usage: dma_bounds [--old-dq-base | --no-back] N1 N2 ...
+//   --old-dq-base  plants the dQ kernel's earlier base row (not clamped to N-1)
+//   --no-back      plants loads that never pull rows past N-1 back
+// Prints the counts and the first violations; exit status 1 if any load violates a check.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "fa_dma.h"
+
+using namespace fa::dma;
+
+static bool g_old_dq = false, g_no_back = false;
+static long g_loads = 0, g_bad = 0;
+
+static void bad(const char* what, const char* kernel, int N, int D, int a, int b, int c, long long v) {
+  if (g_bad < 20)
+    fprintf(stderr, "VIOLATION %s: %s N=%d D=%d (%d,%d,%d) value=%lld\n", what, kernel, N, D, a, b, c, v);
+  ++g_bad;
+}
+
+static uint32_t back_of(int row0, int r, int N, int row_bytes) {
+  return g_no_back ? 0u : past_end_back(row0, r, N, row_bytes);
+}
+
+// one 16-byte load: global byte offset (as the kernel forms it: unsigned 32-bit lane offset minus
+// the pull-back, added to a row base) and its expected value
+static void check_load(const char* k, int N, int D, int row_bytes, int64_t base, uint32_t off, uint32_t back,
+                       int want_row, int want_chunk, int a, int b, int c) {
+  ++g_loads;
+  const uint32_t lane_off = off - back;                  // unsigned, as in the kernel
+  const int64_t src = base + (int64_t)lane_off;
+  if ((int64_t)off - (int64_t)back < 0) bad("lane offset wraps below 0", k, N, D, a, b, c, (long long)off - back);
+  if (src < 0 || src + 16 > (int64_t)N * row_bytes) bad("read outside the head", k, N, D, a, b, c, src);
+  const int64_t want = (int64_t)want_row * row_bytes + 16 * (int64_t)want_chunk;
+  if (src != want) bad("reads the wrong row or chunk", k, N, D, a, b, c, src - want);
+}
+
+// ---- forward, head width 128 ---------------------------------------------------------------
+static void fwd128(int N, bool causal) {
+  const int BR = 256, BC = 64, SLOTS = 4, ROWB = kFwd128RowBytes, TILEB = BC * ROWB;
+  const int VREGION = SLOTS * TILEB, LDS = 2 * SLOTS * TILEB;
+  const int nqt = (N + BR - 1) / BR;
+  for (int qt = 0; qt < nqt; ++qt) {
+    const int kv_end = causal ? (N < (qt + 1) * BR ? N : (qt + 1) * BR) : N;
+    const int nkv = (kv_end + BC - 1) / BC;
+    for (int t = 0; t < nkv; ++t) {
+      const int key0 = t * BC, slot = t & (SLOTS - 1);
+      const bool full = key0 + BC <= N;
+      std::vector<int> hits(2 * TILEB / 16, 0);
+      for (int wave = 0; wave < 8; ++wave)
+        for (int i = 0; i < 2; ++i)
+          for (int lane = 0; lane < 64; ++lane) {
+            const int r = fwd128_row(wave, lane, i);
+            const uint32_t back = full ? 0u : back_of(key0, r, N, ROWB);
+            const int row = key0 + r < N - 1 ? key0 + r : N - 1;
+            const int64_t base = (int64_t)key0 * ROWB;
+            check_load("fwd128 K", N, 128, ROWB, base, fwd128_k_off(wave, lane, i), back, row,
+                       (lane & 15) ^ (r & 15), t, wave, lane);
+            check_load("fwd128 V", N, 128, ROWB, base, fwd128_v_off(wave, lane, i), back, row,
+                       (lane & 15) ^ ((r & 3) << 2), t, wave, lane);
+            const int dk = slot * TILEB + (2 * wave + i) * 1024 + 16 * lane;   // K ring; V at +VREGION
+            if (dk < slot * TILEB || dk + 16 > (slot + 1) * TILEB || dk + VREGION + 16 > LDS)
+              bad("LDS write outside the slot", "fwd128", N, 128, t, wave, lane, dk);
+            if ((dk - slot * TILEB) / ROWB != r || ((dk - slot * TILEB) % ROWB) / 16 != (lane & 15))
+              bad("LDS place is not the loaded row's physical chunk", "fwd128", N, 128, t, wave, lane, dk);
+            ++hits[(dk - slot * TILEB) / 16];
+          }
+      for (int p = 0; p < TILEB / 16; ++p)
+        if (hits[p] != 1) bad("tile place not written exactly once", "fwd128", N, 128, t, p, 0, hits[p]);
+    }
+  }
+}
+
+// ---- backward, dQ kernel (4 waves, 128 queries; 64-key steps of two 32-row sub-tiles) --------
+template <int D>
+static void dq(int N, bool causal) {
+  const int KT = 32 * D, SLOTB = 4 * KT * 2, KB_SUB = 2 * KT / 1024, RB = 2 * D;
+  const int nqt = (N + 127) / 128;
+  for (int qt = 0; qt < nqt; ++qt) {
+    const int kv_end = causal ? (N < (qt + 1) * 128 ? N : (qt + 1) * 128) : N;
+    const int nst = (kv_end + 63) / 64;
+    for (int t = 0; t < nst; ++t) {
+      const int slot = t & 1;
+      for (int wave = 0; wave < 4; ++wave) {
+        const int u0 = 2 * t * 32 + (wave & 1) * 32;       // sub-tile's first key (unclamped)
+        const int row0 = g_old_dq ? u0 : dq_row0(t, wave, N);
+        std::vector<int> hits(2 * KT / 16, 0);
+        for (int i = 0; i < KB_SUB; ++i)
+          for (int lane = 0; lane < 64; ++lane) {
+            const int r = tile_row<D>(i, lane);
+            const int row = u0 + r < N - 1 ? u0 + r : N - 1;
+            check_load("dq", N, D, RB, (int64_t)row0 * RB, tile_off<D>(i, lane), back_of(row0, r, N, RB), row,
+                       (lane % (D / 8)) ^ swz<D>(r), t, wave, lane);
+            const int lo = slot * SLOTB + wave * KT * 2, d = lo + i * 1024 + 16 * lane;
+            if (d + 16 > lo + KT * 2 || d + 16 > 2 * SLOTB) bad("LDS write outside the sub-tile", "dq", N, D, t, wave, d, 0);
+            ++hits[(d - lo) / 16];
+          }
+        for (int p = 0; p < 2 * KT / 16; ++p)
+          if (hits[p] != 1) bad("sub-tile place not written exactly once", "dq", N, D, t, wave, p, hits[p]);
+      }
+    }
+  }
+}
+
+// ---- backward, dK/dV kernel (128 keys; query blocks of 32 rows into 5 slots) ---------------
+template <int D>
+static void dkdv(int N, bool causal) {
+  const int NW = 4, RPW = 2 * (D / 64), KB_TILE = 2 * 32 * D / 1024, TILEB = 2 * 32 * D;
+  const int SLOTB = 2 * TILEB + 512, SLOTS = 5, RB = 2 * D;
+  const int nkb = (N + 127) / 128, nqb = (N + 31) / 32;
+  for (int kblk = 0; kblk < nkb; ++kblk) {
+    const int qb0 = causal ? kblk * 128 / 32 : 0;
+    for (int qb = qb0; qb < nqb; ++qb) {
+      const int row0 = qb * 32;
+      {
+        const int slot = (qb - qb0) % SLOTS;   // block qb0 + j goes to slot j mod 5
+        std::vector<int> hits(SLOTB / 16, 0);
+        for (int lw = 0; lw < NW; ++lw) {
+          const int tile = (lw * RPW) / KB_TILE;   // 0: Q, 1: dO
+          for (int i = 0; i < RPW; ++i) {
+            const int kb = (lw * RPW + i) % KB_TILE;
+            for (int lane = 0; lane < 64; ++lane) {
+              const int r = tile_row<D>(kb, lane);
+              const int row = row0 + r < N - 1 ? row0 + r : N - 1;
+              check_load("dkdv", N, D, RB, (int64_t)row0 * RB, tile_off<D>(kb, lane), back_of(row0, r, N, RB), row,
+                         (lane % (D / 8)) ^ swz<D>(r), qb, lw, lane);
+              const int lo = slot * SLOTB + tile * TILEB, d = lo + kb * 1024 + 16 * lane;
+              if (d + 16 > lo + TILEB) bad("LDS write outside the tile", "dkdv", N, D, qb, lw, d, 0);
+              ++hits[(d - slot * SLOTB) / 16];
+            }
+          }
+          if (lw < 2) {   // 32 log-normalisers (wave 0) or deltas (wave 1), lanes 32..63 repeat
+            for (int lane = 0; lane < 64; ++lane) {
+              ++g_loads;
+              const int lr = lane & 31;
+              const int idx = row0 + (lr < N - 1 - row0 ? lr : N - 1 - row0);
+              if (N - 1 - row0 < 0 || idx < 0 || idx >= N) bad("row statistic outside the head", "dkdv", N, D, qb, lw, lane, idx);
+              const int d = slot * SLOTB + 2 * TILEB + lw * 256 + 4 * lane;
+              if (d + 4 > (slot + 1) * SLOTB) bad("LDS write outside the slot", "dkdv stats", N, D, qb, lw, lane, d);
+            }
+          }
+        }
+        for (int p = 0; p < 2 * TILEB / 16; ++p)
+          if (hits[p] != 1) bad("slot place not written exactly once", "dkdv", N, D, qb, slot, p, hits[p]);
+      }
+    }
+  }
+}
+
+int main(int argc, char** argv) {
+  std::vector<int> Ns;
+  for (int a = 1; a < argc; ++a) {
+    if (!strcmp(argv[a], "--old-dq-base")) g_old_dq = true;
+    else if (!strcmp(argv[a], "--no-back")) g_no_back = true;
+    else Ns.push_back(atoi(argv[a]));
+  }
+  for (int N : Ns) {
+    if (N < 1) continue;
+    for (int causal = 0; causal < 2; ++causal) {
+      fwd128(N, causal);
+      dq<64>(N, causal);
+      dq<128>(N, causal);
+      if (N <= 8192) {   // (the dK/dV walk is quadratic in N; it is covered up to 8192)
+        dkdv<64>(N, causal);
+        dkdv<128>(N, causal);
+      }
+    }
+  }
+  printf("loads checked: %ld, violations: %ld\n", g_loads, g_bad);
+  return g_bad ? 1 : 0;
+}
