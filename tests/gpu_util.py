@@ -46,6 +46,8 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, label: str = "", tol=Non
     stats = {"max": float(err.max()), "mean": float(err.mean())}
     if lse_gpu is not None:
         stats["lse"] = float(np.abs(lse_gpu - lse_ref).max())
+    note(f"  {label}: max err {stats['max']:.3e} (bound {tol['max']:.1e}, ratio {stats['max'] / tol['max']:.3f}), "
+         f"mean err {stats['mean']:.3e}" + (f", lse err {stats['lse']:.3e}" if "lse" in stats else ""))
     assert np.all(np.isfinite(o_gpu)), f"{label}: non-finite output"
     assert stats["max"] <= tol["max"], f"{label}: max abs error {stats['max']:.3e} > {tol['max']}"
     assert stats["mean"] <= tol["mean"], f"{label}: mean abs error {stats['mean']:.3e} > {tol['mean']}"
@@ -61,22 +63,13 @@ def full_parity(t: dict, dtype: str, scale: float, causal: bool, label: str, tol
     return compare(o, l, o_ref, l_ref, dtype, label, tol)
 
 
-def fp32_logit_bound(t: dict, scale: float) -> dict:
-    """fp32 tolerance for scores far larger than the workloads' (|scale| >> 1/sqrt(d)).
-
-    Each fp32 score s_ij = sum_c q_ic k_jc carries a rounding error of at most
-    d * 2^-24 * sum_c |q_ic k_jc| (recursive summation), the softmax turns an error e in
-    the logits into at most 2 * e * max|v| in the output, and the exponent argument adds
-    a few ulps of the logit range. The bound is that, plus the stated 1e-5 floor.
-    """
-    q = np.abs(t["q"].astype(np.float64))
-    k = np.abs(t["k"].astype(np.float64))
-    d = q.shape[-1]
-    dots = np.einsum("bhic,bhjc->bhij", q, k).max()
-    logit_err = abs(scale) * d * 2.0 ** -24 * dots
-    vmax = np.abs(t["v"]).max()
-    o_tol = 1e-5 + 2.0 * vmax * (logit_err + 4 * 2.0 ** -24 * abs(scale) * dots)
-    return {"max": o_tol, "mean": o_tol, "lse": 1e-3}
+def fp32_scaled_tolerance(d: int, scale: float) -> dict:
+    """fp32 tolerance for logits larger than the workloads'. The stated 1e-5 holds at scale
+    1/sqrt(d); the rounding of the logits and of the exponent arguments grows in proportion to
+    the logits, so the output bound is scaled by the logit amplification |scale| sqrt(d) (never
+    below 1). The lse bound stays 1e-3."""
+    f = max(1.0, abs(scale) * math.sqrt(d))
+    return {"max": 1e-5 * f, "mean": 1e-5 * f, "lse": 1e-3}
 
 
 def sampled_parity(w: inputs.Workload, rows_per_head: int, label: str):
