@@ -34,14 +34,16 @@ MUTANTS = [
     ("attention.py", "r = _rows_for(rows, b, h, N)", "r = _rows_for(rows, 0, 0, N)", "per-head rows ignored"),
     ("attention.py", "return w / w.sum(axis=1, keepdims=True)", "return w / w.sum(axis=0, keepdims=True)",
      "probabilities normalised over queries"),
-    ("online.py", "factor = 0.0 if m == -math.inf else math.exp(m - m_new)", "factor = 1.0",
-     "block merge never rescales"),
-    ("online.py", "total = total * factor", "total = total", "block merge rescales only the numerator"),
-    ("online.py", "total = rescale * total + w", "total = total + w", "scalar recurrence drops the rescale"),
-    ("online.py", "weighted = rescale * weighted + w * val", "weighted = rescale * weighted + val",
-     "scalar recurrence drops the weight"),
-    ("online.py", "running_sum = running_sum * math.exp(running_max - new_max)",
-     "running_sum = running_sum", "normaliser never rescales"),
+    ("online.py", "wa = 0.0 if a.m == -math.inf else math.exp(a.m - m)", "wa = 0.0 if a.m == -math.inf else 1.0",
+     "merge never rescales the running side"),
+    ("online.py", "wb = 0.0 if b.m == -math.inf else math.exp(b.m - m)", "wb = 1.0",
+     "merge never rescales the incoming block"),
+    ("online.py", "return State(m, wa * a.l + wb * b.l, wa * a.u + wb * b.u)",
+     "return State(m, a.l + wb * b.l, wa * a.u + wb * b.u)", "merge rescales only the numerator"),
+    ("online.py", "m = max(a.m, b.m)", "m = min(a.m, b.m)", "merge keeps the smaller max"),
+    ("online.py", "p = np.exp(s - m)", "p = np.exp(s)", "block state without the max subtraction"),
+    ("online.py", "return State(m, float(p.sum()), p @ vals)", "return State(m, float(p.sum()), vals.sum(axis=0))",
+     "block state drops the weights of the values"),
 ]
 
 
