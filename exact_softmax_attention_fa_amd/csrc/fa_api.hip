@@ -12,10 +12,11 @@
 namespace {
 
 // Checks shared by both entry points. Runs before any HIP call; a rejected call writes
-// nothing. On success fills `args` and the padded head width.
+// nothing. `br` is the query rows per workgroup of the kernel that will run. On success fills
+// `args` and the padded head width.
 int validate(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int N, int d, float scale, int causal, size_t elem,
-             int (*rows_per_block)(int), fa::FwdArgs* args, int* d_pad) {
+             int br, fa::FwdArgs* args, int* d_pad) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -42,7 +43,6 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
   if (lse != nullptr && overlap(lse, lse_bytes, o, bytes)) return FA_ERR_INVALID_ARG;
 
   const int dp = d <= 64 ? 64 : (d <= 128 ? 128 : 256);
-  const int br = rows_per_block(d);
   const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
   if ((int64_t)B * H * n_qtiles > INT_MAX) return FA_ERR_UNSUPPORTED;
 
@@ -67,6 +67,7 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
 }
 
 constexpr int kMaxSplits = 64;
+constexpr int kMinColumnKeys = 1024;   // shortest key column of the default split
 
 using fa::SplitPlan;
 
@@ -86,9 +87,17 @@ int plan_split(int B, int H, int N, int d, int dtype, int causal, int num_splits
   const int64_t base = (int64_t)B * H * (((int64_t)N + rows - 1) / rows);   // workgroups of one column
   int64_t want = num_splits;
   if (want == 0) {
-    // Library choice: enough columns for about one workgroup per CU of the 256, never more
-    // columns than key tiles.
-    want = base >= 256 ? 1 : (256 + base - 1) / base;
+    // Library choice, for grids of fewer than one workgroup per CU of the 256 (larger grids
+    // keep one column): about 256 workgroups without the mask. Under the causal mask the key
+    // ranges of the query tiles grow from one tile to all of them, so the last query tile
+    // would finish long after the rest; columns of fewer keys (about 2048 workgroups, of which
+    // the ones past the diagonal exit at once) even that out. Columns keep at least
+    // kMinColumnKeys keys: below that, writing and merging the partial states costs more than
+    // the spread gains.
+    const int64_t target = causal ? 2048 : 256;
+    const int64_t by_len = ((int64_t)N + kMinColumnKeys - 1) / kMinColumnKeys;
+    want = base >= 256 ? 1 : (target + base - 1) / base;
+    if (want > by_len) want = by_len;
   }
   want = want < 1 ? 1 : (want > kMaxSplits ? kMaxSplits : want);
   if (want > tiles) want = tiles;
@@ -129,7 +138,7 @@ int splitkv_check(const void* q, const void* k, const void* v, void* o, float* l
   int d_pad = 0;
   const bool bf = dtype == FA_BF16;
   return validate(q, k, v, o, lse, B, H, N, d, scale, causal, bf ? 2 : 4,
-                  bf ? fa::bf16_split_rows_per_block : fa::f32_rows_per_block, args, &d_pad);
+                  bf ? fa::bf16_split_rows_per_block(plan->d_pad) : fa::f32_rows_per_block(d), args, &d_pad);
 }
 
 int splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
@@ -160,7 +169,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   fa::FwdArgs args;
   int d_pad = 0;
   const int st = validate(q, k, v, o, lse, B, H, N, d, scale, causal, 2,
-                          fa::bf16_rows_per_block, &args, &d_pad);
+                          fa::bf16_rows_per_block(d, (int64_t)B * H, N), &args, &d_pad);
   if (st != FA_OK) return st;
   return fa::launch_bf16(args, d_pad, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -170,7 +179,7 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
   fa::FwdArgs args;
   int d_pad = 0;
   const int st = validate(q, k, v, o, lse, B, H, N, d, scale, causal, 4,
-                          fa::f32_rows_per_block, &args, &d_pad);
+                          fa::f32_rows_per_block(d), &args, &d_pad);
   if (st != FA_OK) return st;
   return fa::launch_f32(args, d_pad, causal != 0, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -153,7 +153,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int TILEB = 2 * QT;         // bytes per tile
   constexpr int SLOTB = 2 * TILEB + 512;   // Q tile, dO tile, 64 floats of log-normaliser, 64 of delta
   constexpr int SLOTS = 5;
-  constexpr int NC = D / 8;             // 16-byte chunks per row
   constexpr int IPW = D / 64;           // 1 KiB loads per wave per block (Q and dO: 2 TILEB)
   constexpr int KB_TILE = TILEB / 1024; // 1 KiB regions per tile
   static_assert(2 * KB_TILE == 8 * IPW, "8 waves load the two tiles");
@@ -430,7 +429,6 @@ void bwd_dq_kernel(BwdArgs a) {
   // in the other, loaded straight from global memory at the start of step t.
   constexpr int KT = BLK * D;           // one swizzled sub-tile (elements)
   constexpr int SLOT = 4 * KT;          // elements per slot
-  constexpr int NC = D / 8;             // 16-byte chunks per row
   constexpr int KB_SUB = 2 * KT / 1024; // 1 KiB regions per sub-tile: one wave loads one sub-tile
   static_assert(KB_SUB * 1024 == 2 * KT, "sub-tile size");
 

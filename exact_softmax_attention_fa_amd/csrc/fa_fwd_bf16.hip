@@ -90,23 +90,47 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max r
 #ifndef FA_BF16_D128_WPE
 #define FA_BF16_D128_WPE 2
 #endif
+#ifndef FA_BF16_D64W_NW
+#define FA_BF16_D64W_NW 8
+#endif
+// Grids of at least this many workgroups of the wide head-width-64 configuration use it.
+#ifndef FA_BF16_D64W_MIN_WGS
+#define FA_BF16_D64W_MIN_WGS 256
+#endif
 // NW counts the waves of one key group; a workgroup runs SPLIT key groups (MAXSPLIT at most)
-// over the same queries and merges them at the end.
-template <int D> struct Cfg;
+// over the same queries and merges them at the end. D is the padded head width.
+template <int D_> struct Cfg;
 template <> struct Cfg<64> {
+  static constexpr int D = 64;
   static constexpr int QW = FA_BF16_D64_QW, NW = FA_BF16_D64_NW, BC = FA_BF16_D64_BC, WPE = FA_BF16_D64_WPE;
   static constexpr int MAXSPLIT = 4;
 };
+// Head widths up to 64 on large grids: 8 waves share each K/V tile (four times fewer tile
+// loads per query than the 2-wave blocks), no key split. The 2-wave blocks with their key split
+// stay the choice for small grids, where the wide blocks would leave CUs idle.
+struct CfgD64Wide {
+  static constexpr int D = 64;
+  static constexpr int QW = 1, NW = FA_BF16_D64W_NW, BC = 64, WPE = 2;
+  static constexpr int MAXSPLIT = 1;
+};
 template <> struct Cfg<128> {
+  static constexpr int D = 128;
   static constexpr int QW = FA_BF16_D128_QW, NW = FA_BF16_D128_NW, BC = FA_BF16_D128_BC, WPE = FA_BF16_D128_WPE;
   static constexpr int MAXSPLIT = 1;
 };
 // head widths 129..256: one wave per SIMD (the 256-wide accumulators and operands need more
 // than 256 registers), 4 waves of 32 query rows
 template <> struct Cfg<256> {
+  static constexpr int D = 256;
   static constexpr int QW = 1, NW = 4, BC = 32, WPE = 1;
   static constexpr int MAXSPLIT = 1;
 };
+
+// Whether a head-width-64 forward call over BH heads of N queries runs the wide blocks.
+bool d64_wide(int64_t BH, int N) {
+  constexpr int rows = CfgD64Wide::NW * CfgD64Wide::QW * 32;
+  return BH * (((int64_t)N + rows - 1) / rows) >= FA_BF16_D64W_MIN_WGS;
+}
 
 __device__ __forceinline__ float pair_max(float x) {
   // lanes l and l^32 exchange x; after the swap each lane holds both halves' values
@@ -262,14 +286,14 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
 
 // Minimum waves per SIMD the register allocation must allow: a workgroup of two waves or fewer
 // may use the whole register file (larger ones keep the configured occupancy).
-template <int D, int SPLIT> constexpr int min_waves_per_simd() { return Cfg<D>::NW * SPLIT <= 2 ? 1 : Cfg<D>::WPE; }
+template <class C, int SPLIT> constexpr int min_waves_per_simd() { return C::NW * SPLIT <= 2 ? 1 : C::WPE; }
 
 // PARTIAL: the workgroup covers only the keys of its split column (blockIdx.y) and writes its
 // partial state (m, l, u) to the workspace instead of o and lse; a merge pass combines them.
-template <int D, bool CAUSAL, bool FULLD, int SPLIT, bool PARTIAL>
-__global__ __launch_bounds__(Cfg<D>::NW * SPLIT * 64, (min_waves_per_simd<D, SPLIT>()))
+template <class C, bool CAUSAL, bool FULLD, int SPLIT, bool PARTIAL>
+__global__ __launch_bounds__(C::NW * SPLIT * 64, (min_waves_per_simd<C, SPLIT>()))
 void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int QW = Cfg<D>::QW, NW = Cfg<D>::NW, BC = Cfg<D>::BC;
+  constexpr int D = C::D, QW = C::QW, NW = C::NW, BC = C::BC;
   constexpr int NT = NW * SPLIT * 64;
   constexpr int BR = NW * QW * 32;
   constexpr int KP = D + 8;    // K row pitch (elements): conflict-free 16-byte reads of 32 rows
@@ -544,62 +568,68 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, int SPLIT, bool PARTIAL>
+template <class C, bool CAUSAL, int SPLIT, bool PARTIAL>
 hipError_t launch_split(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
   const dim3 grid((unsigned)(a.BH * a.n_qtiles), (unsigned)ncol);
-  const dim3 block(Cfg<D>::NW * SPLIT * 64);
+  const dim3 block(C::NW * SPLIT * 64);
   // (head width exactly 128 runs on the tuned kernel in a single pass, so the generic 128-wide
   // kernel is built for full rows only where the split pass uses it)
-  if constexpr (D != 128 || PARTIAL) {
+  if constexpr (C::D != 128 || PARTIAL) {
     if (fulld) {
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, SPLIT, PARTIAL>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<C, CAUSAL, true, SPLIT, PARTIAL>), grid, block, 0, stream, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, SPLIT, PARTIAL>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<C, CAUSAL, false, SPLIT, PARTIAL>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 // Key groups per workgroup: split the key range as far as MAXSPLIT allows when the grid has
 // at most one workgroup per CU, as long as every group still gets at least two tiles.
 // `keys` is the length of one workgroup's key range, `ncol` the number of split columns.
-template <int D>
+template <class C>
 int choose_split(const FwdArgs& a, int keys, int ncol) {
   const long long wgs = (long long)a.BH * a.n_qtiles * ncol;
-  const int nkv = (keys + Cfg<D>::BC - 1) / Cfg<D>::BC;
+  const int nkv = (keys + C::BC - 1) / C::BC;
   int split = 1;
-  while (split * 2 <= Cfg<D>::MAXSPLIT && wgs <= FA_SPLIT_MAX_WGS && nkv >= 2 * split * 2) split *= 2;
+  while (split * 2 <= C::MAXSPLIT && wgs <= FA_SPLIT_MAX_WGS && nkv >= 2 * split * 2) split *= 2;
   return split;
 }
 
-template <int D, bool CAUSAL, bool PARTIAL>
+template <class C, bool CAUSAL, bool PARTIAL>
 hipError_t launch_one(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
-  if constexpr (Cfg<D>::MAXSPLIT >= 4) {
-    const int split = choose_split<D>(a, PARTIAL ? a.kv_chunk : a.N, ncol);
-    if (split == 4) return launch_split<D, CAUSAL, 4, PARTIAL>(a, fulld, ncol, stream);
-    if (split == 2) return launch_split<D, CAUSAL, 2, PARTIAL>(a, fulld, ncol, stream);
+  if constexpr (C::MAXSPLIT >= 4) {
+    const int split = choose_split<C>(a, PARTIAL ? a.kv_chunk : a.N, ncol);
+    if (split == 4) return launch_split<C, CAUSAL, 4, PARTIAL>(a, fulld, ncol, stream);
+    if (split == 2) return launch_split<C, CAUSAL, 2, PARTIAL>(a, fulld, ncol, stream);
   }
-  return launch_split<D, CAUSAL, 1, PARTIAL>(a, fulld, ncol, stream);
+  return launch_split<C, CAUSAL, 1, PARTIAL>(a, fulld, ncol, stream);
 }
 
+template <class C, bool PARTIAL>
+hipError_t launch_causal(const FwdArgs& a, bool fulld, bool causal, int ncol, hipStream_t stream) {
+  return causal ? launch_one<C, true, PARTIAL>(a, fulld, ncol, stream)
+                : launch_one<C, false, PARTIAL>(a, fulld, ncol, stream);
+}
+
+// The split pass (PARTIAL) always runs the narrow configurations; the single pass at head
+// width 64 takes the wide blocks where d64_wide says so (its grid was sized for them).
 template <bool PARTIAL>
 hipError_t launch_generic(const FwdArgs& a, int d_pad, bool causal, int ncol, hipStream_t stream) {
   const bool fulld = (a.d == d_pad);
-  if (d_pad == 64)
-    return causal ? launch_one<64, true, PARTIAL>(a, fulld, ncol, stream)
-                  : launch_one<64, false, PARTIAL>(a, fulld, ncol, stream);
-  if (d_pad == 128)
-    return causal ? launch_one<128, true, PARTIAL>(a, fulld, ncol, stream)
-                  : launch_one<128, false, PARTIAL>(a, fulld, ncol, stream);
-  return causal ? launch_one<256, true, PARTIAL>(a, fulld, ncol, stream)
-                : launch_one<256, false, PARTIAL>(a, fulld, ncol, stream);
+  if (d_pad == 64) {
+    if (!PARTIAL && d64_wide(a.BH, a.N)) return launch_causal<CfgD64Wide, false>(a, fulld, causal, ncol, stream);
+    return launch_causal<Cfg<64>, PARTIAL>(a, fulld, causal, ncol, stream);
+  }
+  if (d_pad == 128) return launch_causal<Cfg<128>, PARTIAL>(a, fulld, causal, ncol, stream);
+  return launch_causal<Cfg<256>, PARTIAL>(a, fulld, causal, ncol, stream);
 }
 
 }  // namespace
 
-int bf16_rows_per_block(int d) {
+int bf16_rows_per_block(int d, int64_t BH, int N) {
   if (d == 128) return bf16_d128_rows_per_block();
-  if (d <= 64) return Cfg<64>::NW * Cfg<64>::QW * 32;
+  if (d <= 64) return d64_wide(BH, N) ? CfgD64Wide::NW * CfgD64Wide::QW * 32 : Cfg<64>::NW * Cfg<64>::QW * 32;
   if (d <= 128) return Cfg<128>::NW * Cfg<128>::QW * 32;
   return Cfg<256>::NW * Cfg<256>::QW * 32;
 }

@@ -32,8 +32,9 @@ struct FwdArgs {
 };
 
 // Rows of queries per workgroup of the kernel that will run for head width d (host needs it
-// for the grid).
-int bf16_rows_per_block(int d);
+// for the grid). The bf16 choice at head widths up to 64 also depends on the grid: BH heads
+// (B * H) of N queries.
+int bf16_rows_per_block(int d, int64_t BH, int N);
 int f32_rows_per_block(int d);
 
 // Enqueue one forward pass. d_pad (64, 128 or 256) is the padded head width of the generic

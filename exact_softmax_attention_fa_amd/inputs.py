@@ -111,6 +111,9 @@ EXTRA_WORKLOADS = {
     "fwd_bf16_b1_h1_n32768_d128_causal": Workload(
         "fwd_bf16_b1_h1_n32768_d128_causal", 1, 1, 32768, 128, "bf16", True, 1202,
         note="one head of the long-context shape, bf16 N(0,1) inputs, causal"),
+    "fwd_bf16_b1_h1_n8192_d128_causal": Workload(
+        "fwd_bf16_b1_h1_n8192_d128_causal", 1, 1, 8192, 128, "bf16", True, 1203,
+        note="one head of the headline shape, bf16 N(0,1) inputs, causal"),
 }
 ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
 

@@ -20,7 +20,10 @@ int g_last_ncol = 0;
 
 // ---- stubs of the kernel side (same row and tile geometry as the kernels) -------------------
 namespace fa {
-int bf16_rows_per_block(int d) { return d == 128 ? 256 : (d <= 64 ? 64 : (d <= 128 ? 256 : 128)); }
+int bf16_rows_per_block(int d, int64_t BH, int N) {
+  if (d <= 64) return BH * (((int64_t)N + 255) / 256) >= 256 ? 256 : 64;
+  return d == 128 ? 256 : (d <= 128 ? 256 : 128);
+}
 int f32_rows_per_block(int d) { return d <= 64 ? 32 : (d <= 128 ? 64 : 128); }
 int bf16_d128_rows_per_block() { return 256; }
 int bf16_split_rows_per_block(int d_pad) { return d_pad <= 64 ? 64 : (d_pad <= 128 ? 256 : 128); }
@@ -115,7 +118,7 @@ int main() {
     fprintf(stderr, "FAIL headline launch arguments: BH=%d n_qtiles=%d\n", g_last.BH, g_last.n_qtiles);
     ++g_fail;
   }
-  expect("split fp32 256", fa_fwd_splitkv(q, k, v, o, lse, 1, 1, 256, 64, 0.125f, 0, FA_F32, 0, (void*)(8 * G),
+  expect("split fp32 256", fa_fwd_splitkv(q, k, v, o, lse, 1, 1, 256, 64, 0.125f, 0, FA_F32, 8, (void*)(8 * G),
                                           1 << 30, nullptr), FA_OK);
   if (g_last_ncol != 8 || g_last.kv_chunk != 32 || (uintptr_t)g_last.part_u != 8 * G) {
     fprintf(stderr, "FAIL split launch arguments: ncol=%d kv_chunk=%d\n", g_last_ncol, g_last.kv_chunk);

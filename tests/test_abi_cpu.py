@@ -146,14 +146,15 @@ def plan(B=1, H=1, N=256, d=64, dtype=fa.FA_F32, causal=0, num_splits=0):
     return fa.fa_fwd_splitkv_plan(B, H, N, d, dtype, causal, num_splits)
 
 
-def expected_plan(B, H, N, d, dtype, num_splits, tile, rows):
+def expected_plan(B, H, N, d, dtype, num_splits, tile, rows, causal=0):
     """The plan rule restated: at most one column per key tile, columns of whole tiles, no
-    empty column; the default aims at about one workgroup per CU (256)."""
+    empty column; below 256 workgroups the default aims at 256 of them (2048 under the causal
+    mask, where the columns past the diagonal exit at once), in columns of at least 1024 keys."""
     import math
     dp = 64 if d <= 64 else (128 if d <= 128 else 256)
     tiles = math.ceil(N / tile)
     base = B * H * math.ceil(N / rows)
-    want = num_splits or (1 if base >= 256 else math.ceil(256 / base))
+    want = num_splits or (1 if base >= 256 else min(math.ceil((2048 if causal else 256) / base), math.ceil(N / 1024)))
     want = max(1, min(want, 64, tiles))
     chunk = math.ceil(tiles / want) * tile
     ns = math.ceil(N / chunk)
@@ -164,8 +165,9 @@ def expected_plan(B, H, N, d, dtype, num_splits, tile, rows):
     return ns, (u + 255) // 256 * 256 + rows_all * 8
 
 
+@pytest.mark.parametrize("causal", [0, 1])
 @pytest.mark.parametrize("B,H,N,d,dtype,ns", [
-    (1, 1, 256, 64, fa.FA_F32, 0),      # the fp32 single-head workload: 8 query tiles, 8 key tiles
+    (1, 1, 256, 64, fa.FA_F32, 0),      # the fp32 single-head workload: too few keys to split
     (1, 1, 256, 64, fa.FA_F32, 3),
     (1, 1, 256, 64, fa.FA_F32, 64),     # clamped to the 8 key tiles
     (1, 1, 8192, 128, fa.FA_BF16, 0),
@@ -174,16 +176,19 @@ def expected_plan(B, H, N, d, dtype, num_splits, tile, rows):
     (1, 2, 1000, 96, fa.FA_BF16, 5),
     (1, 1, 33, 200, fa.FA_F32, 4),      # 2 key tiles of 32
     (1, 1, 1, 64, fa.FA_BF16, 8),       # one key: one column
+    (1, 1, 32768, 128, fa.FA_BF16, 0),  # 128 workgroups: 2 columns, 16 under the causal mask
+    (1, 1, 3000, 64, fa.FA_BF16, 0),    # 3 columns at most (1024 keys or more each)
+    (1, 3, 4000, 64, fa.FA_BF16, 0),
 ])
-def test_splitkv_plan(lib, B, H, N, d, dtype, ns):
-    st, nsplit, wbytes = plan(B, H, N, d, dtype, 0, ns)
+def test_splitkv_plan(lib, B, H, N, d, dtype, ns, causal):
+    st, nsplit, wbytes = plan(B, H, N, d, dtype, causal, ns)
     assert st == fa.FA_OK
     if dtype == fa.FA_F32:
         tile, rows = 32, {64: 32, 128: 64, 256: 128}[64 if d <= 64 else (128 if d <= 128 else 256)]
     else:
         tile = 32 if d > 128 else 64
         rows = {64: 64, 128: 256, 256: 128}[64 if d <= 64 else (128 if d <= 128 else 256)]
-    assert (nsplit, wbytes) == expected_plan(B, H, N, d, dtype, ns, tile, rows)
+    assert (nsplit, wbytes) == expected_plan(B, H, N, d, dtype, ns, tile, rows, causal)
 
 
 @pytest.mark.parametrize("kwargs,status", [
