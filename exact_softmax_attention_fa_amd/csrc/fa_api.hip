@@ -18,6 +18,9 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int N, int d, float scale, int causal, size_t elem,
              int br, fa::FwdArgs* args, int* d_pad) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
+  // rows move in 16-byte pieces: q, k, v, o 16-byte aligned, lse 4-byte aligned
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_INVALID_ARG;
+  if ((uintptr_t)lse & 3) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
@@ -222,6 +225,11 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   void* outs[4] = {dq, dk, dv, delta};
   for (const void* p : ins) if (p == nullptr) return FA_ERR_INVALID_ARG;
   for (const void* p : outs) if (p == nullptr) return FA_ERR_INVALID_ARG;
+  // 16-byte aligned row arrays, 4-byte aligned row statistics
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)lse | (uintptr_t)delta) & 3) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;

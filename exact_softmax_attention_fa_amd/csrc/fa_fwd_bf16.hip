@@ -148,13 +148,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
-// 8 consecutive bf16 of one row, zero outside [0, d) (generic head width). The loads are
-// unconditional (column clamped) so that they issue together.
-__device__ __forceinline__ u32x4 load8_masked(const uint16_t* row, int col, int d) {
+// How a kernel reads rows of q, k, v and writes rows of o (d = stored head width, D = padded):
+//   LD_FULL  d == D: whole 16-byte chunks
+//   LD_VEC8  d a multiple of 8: a chunk lies wholly inside the row or wholly past its end, so
+//            chunks are read or written whole, or skipped (zero)
+//   LD_ELEM  any other d: element by element, columns past d read as zero
+enum { LD_FULL = 0, LD_VEC8 = 1, LD_ELEM = 2 };
+
+// 8 consecutive bf16 of one row, zero outside [0, d) (generic head width). The row starts at
+// element row0 of base; elements are addressed by 32-bit indices off the uniform base, so that
+// no 64-bit address per element stays live. The loads are unconditional (column clamped) so
+// that they issue together.
+__device__ __forceinline__ u32x4 load8_masked(const uint16_t* base, uint32_t row0, int col, int d) {
   uint16_t e[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const uint16_t x = row[min(col + t, d - 1)];
+    const uint16_t x = base[row0 + (uint32_t)min(col + t, d - 1)];
     e[t] = (col + t < d) ? x : (uint16_t)0;
   }
   u32x4 r;
@@ -166,21 +175,24 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t* row, int col, int 
 }
 
 // Everything one wave does with one K/V tile in LDS: S^T = K Q^T, the online-softmax
-// update of its QW query blocks, and O^T += V^T P^T. MASKED selects the slower path that
-// hides keys >= N and, when causal, keys past each query.
-template <int D, int QW, int BC, int KP, int VP, bool MASKED, bool CAUSAL>
+// update of its QW query blocks, and O^T += V^T P^T. `masked` (uniform over the wave) hides
+// keys >= N and, when causal, keys past each query, by setting their scores to -inf before
+// the shared update: sl2 > 0, so the tile maximum max(s) * sl2 equals max(s * sl2) and
+// exp2(fma(-inf, sl2, -m)) = 0. One update path for both kinds of tile keeps a single copy
+// of the accumulators in the loops that mix them.
+template <int D, int QW, int BC, int KP, int VP, bool CAUSAL>
 __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
                                           const u32x4 (&qf)[QW][D / 16], f32x16 (&acc)[QW][D / 32],
                                           float (&m_run)[QW], float (&l_run)[QW],
                                           int key0, int N, int wq_lo, float sl2, int lr, int hh,
-                                          int tr_row, int tr_col) {
+                                          int tr_row, int tr_col, bool masked) {
   // ---- S^T = K Q^T : per 32-key block, all K operands are read before the MFMA chain ----
   f32x16 s[QW][BC / 32];
 #pragma unroll
   for (int kb = 0; kb < BC / 32; ++kb) {
     // (head widths up to 128: all K operands of the block are read before the MFMA chain;
     // wider heads read them as the chain goes, to bound the registers)
-    constexpr int KOPS = D <= 128 ? D / 16 : 1;
+    constexpr int KOPS = D <= 128 ? D / 16 : 1;   // (unused for wider heads)
     u32x4 kop[KOPS];
     const uint16_t* krow = Ks + (kb * 32 + lr) * KP + 8 * hh;
     if constexpr (D <= 128) {
@@ -190,11 +202,25 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
 #pragma unroll
     for (int qb = 0; qb < QW; ++qb) {
       f32x16 c = {};
+      if constexpr (D <= 128) {
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const u32x4 kv = D <= 128 ? kop[kk % KOPS] : *(const u32x4*)(krow + 16 * kk);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv),
-                                                    __builtin_bit_cast(bf16x8, qf[qb][kk]), c, 0, 0, 0);
+        for (int kk = 0; kk < D / 16; ++kk)
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kop[kk]),
+                                                      __builtin_bit_cast(bf16x8, qf[qb][kk]), c, 0, 0, 0);
+      } else {
+        // two operands in flight; the scheduling barriers keep the compiler from hoisting
+        // every read of the chain to its start
+        u32x4 k0 = *(const u32x4*)krow, k1 = *(const u32x4*)(krow + 16);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const u32x4 kv = k0;
+          k0 = k1;
+          if (kk + 2 < D / 16) k1 = *(const u32x4*)(krow + 16 * (kk + 2));
+          __builtin_amdgcn_sched_barrier(0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                      __builtin_bit_cast(bf16x8, qf[qb][kk]), c, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       s[qb][kb] = c;
     }
@@ -205,41 +231,38 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
 #pragma unroll
   for (int qb = 0; qb < QW; ++qb) {
     const int qi = wq_lo + qb * 32 + lr;
-    float mt;
-    if (MASKED) {
-      mt = -INFINITY;
+    if (masked) {
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const bool dead = key >= N || (CAUSAL && key > qi);
-          const float t = dead ? -INFINITY : s[qb][kb][i] * sl2;
-          s[qb][kb][i] = t;
-          mt = fmaxf(mt, t);
+          if (key >= N || (CAUSAL && key > qi)) s[qb][kb][i] = -INFINITY;
         }
-    } else {
-      float m0 = s[qb][0][0], m1 = s[qb][0][1];
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2) {
-          m0 = fmaxf(m0, s[qb][kb][i]);
-          m1 = fmaxf(m1, s[qb][kb][i + 1]);
-        }
-      mt = fmaxf(m0, m1) * sl2;
     }
-    mt = pair_max(mt);
+    float m0 = s[qb][0][0], m1 = s[qb][0][1];
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2) {
+        m0 = fmaxf(m0, s[qb][kb][i]);
+        m1 = fmaxf(m1, s[qb][kb][i + 1]);
+      }
+    float mt = pair_max(fmaxf(m0, m1) * sl2);
     const float m_new = fmaxf(m_run[qb], mt);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run[qb] + kRescaleThreshold)) {
       const float alpha = exp2f(m_run[qb] - m_new);  // 0 while m_run is -inf
       l_run[qb] *= alpha;
       // In-place multiply: tying each output to its input register keeps the compiler from
-      // copying the whole accumulator to merge the taken and not-taken paths.
+      // copying the whole accumulator to merge the taken and not-taken paths. (The 256-wide
+      // accumulators live in AGPRs, which the VGPR constraint would force out of them.)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) asm("v_mul_f32 %0, %0, %1" : "+v"(acc[qb][dt][i]) : "v"(alpha));
+        for (int i = 0; i < 16; ++i) {
+          if constexpr (D <= 128) asm("v_mul_f32 %0, %0, %1" : "+v"(acc[qb][dt][i]) : "v"(alpha));
+          else acc[qb][dt][i] *= alpha;
+        }
       m_run[qb] = m_new;
     }
     const float msub = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
@@ -249,8 +272,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
       float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = MASKED ? __builtin_amdgcn_exp2f(s[qb][kb][i] - msub)
-                      : __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], sl2, -msub));
+        p[i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], sl2, -msub));
         ls[i & 3] += p[i];
       }
 #pragma unroll
@@ -267,19 +289,41 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
   }
 
   // ---- O^T += V^T P^T --------------------------------------------------------------------
+  auto v_operand = [&](int dt, int c16) __attribute__((always_inline)) {
+    const uint16_t* base = Vs + (c16 * 16 + tr_row) * VP + dt * 32 + tr_col;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * VP));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+    return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
+  };
+  if constexpr (D <= 128) {
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
+    for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-    for (int c16 = 0; c16 < BC / 16; ++c16) {
-      const uint16_t* base = Vs + (c16 * 16 + tr_row) * VP + dt * 32 + tr_col;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * VP));
-      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-      const u32x4 av = {lo2[0], lo2[1], hi2[0], hi2[1]};
+      for (int c16 = 0; c16 < BC / 16; ++c16) {
+        const u32x4 av = v_operand(dt, c16);
+#pragma unroll
+        for (int qb = 0; qb < QW; ++qb)
+          acc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pb[qb][c16]), acc[qb][dt], 0, 0, 0);
+      }
+    }
+  } else {
+    // steps st = (dt, c16) in order, two operands in flight (as in the S chain above)
+    constexpr int ST = (D / 32) * (BC / 16);
+    u32x4 v0 = v_operand(0, 0), v1 = v_operand(1 / (BC / 16), 1 % (BC / 16));
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int dt = st / (BC / 16), c16 = st % (BC / 16);
+      const u32x4 av = v0;
+      v0 = v1;
+      if (st + 2 < ST) v1 = v_operand((st + 2) / (BC / 16), (st + 2) % (BC / 16));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int qb = 0; qb < QW; ++qb)
         acc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pb[qb][c16]), acc[qb][dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -290,7 +334,7 @@ template <class C, int SPLIT> constexpr int min_waves_per_simd() { return C::NW 
 
 // PARTIAL: the workgroup covers only the keys of its split column (blockIdx.y) and writes its
 // partial state (m, l, u) to the workspace instead of o and lse; a merge pass combines them.
-template <class C, bool CAUSAL, bool FULLD, int SPLIT, bool PARTIAL>
+template <class C, bool CAUSAL, int LD, int SPLIT, bool PARTIAL>
 __global__ __launch_bounds__(C::NW * SPLIT * 64, (min_waves_per_simd<C, SPLIT>()))
 void fwd_bf16_kernel(FwdArgs a) {
   constexpr int D = C::D, QW = C::QW, NW = C::NW, BC = C::BC;
@@ -343,12 +387,15 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QW; ++qb) {
     const int qi = wq_lo + qb * 32 + lr;
-    const uint16_t* qrow = Qh + (size_t)min(qi, N - 1) * d;
+    const uint32_t qrow0 = (uint32_t)min(qi, N - 1) * (uint32_t)d;
+    const uint16_t* qrow = Qh + qrow0;
     const uint32_t keep = qi < N ? 0xffffffffu : 0u;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const int col = 16 * kk + 8 * hh;
-      const u32x4 x = FULLD ? *(const u32x4*)(qrow + col) : load8_masked(qrow, col, d);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (LD == LD_FULL || (LD == LD_VEC8 && col < d)) x = *(const u32x4*)(qrow + col);
+      else if (LD == LD_ELEM) x = load8_masked(Qh, qrow0, col, d);
       qf[qb][kk] = (x & keep) ^ negmask;
     }
   }
@@ -383,21 +430,30 @@ void fwd_bf16_kernel(FwdArgs a) {
   // step `it` stages tiles it*SPLIT .. it*SPLIT + SPLIT-1 (one per key group)
   auto gload = [&](int it) {
     const int key_lo = (t_beg + it * SPLIT) * BC;
-    const bool whole = FULLD && key_lo + SPLIT * BC <= N;   // no bounds checks needed
+    const bool whole = LD != LD_ELEM && key_lo + SPLIT * BC <= N;   // every staged key exists
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + r * NT;
       const int row = c / (D / 8);      // row within the SPLIT*BC staged keys
       const int col = (c % (D / 8)) * 8;
       const int key = key_lo + row;
-      if (whole) {
-        kreg[r] = *(const u32x4*)(Kh + (size_t)key * d + col);
-        vreg[r] = *(const u32x4*)(Vh + (size_t)key * d + col);
+      // one 32-bit element offset serves K and V (N * d < 2^31), so that the loop keeps no
+      // 64-bit address per chunk live
+      const uint32_t e = (uint32_t)key * (uint32_t)d + (uint32_t)col;
+      if (whole && LD == LD_FULL) {
+        kreg[r] = *(const u32x4*)(Kh + e);
+        vreg[r] = *(const u32x4*)(Vh + e);
       } else {
         u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-        if (key < N) {
-          kx = load8_masked(Kh + (size_t)key * d, col, d);
-          vx = load8_masked(Vh + (size_t)key * d, col, d);
+        if (LD == LD_VEC8) {
+          if ((whole || key < N) && col < d) {
+            kx = *(const u32x4*)(Kh + e);
+            vx = *(const u32x4*)(Vh + e);
+          }
+        } else if (key < N) {
+          const uint32_t row0 = (uint32_t)key * (uint32_t)d;
+          kx = LD == LD_FULL ? *(const u32x4*)(Kh + e) : load8_masked(Kh, row0, col, d);
+          vx = LD == LD_FULL ? *(const u32x4*)(Vh + e) : load8_masked(Vh, row0, col, d);
         }
         kreg[r] = kx;
         vreg[r] = vx;
@@ -444,9 +500,8 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int buf = it & 1;
     if (it + 1 < nit) gload(it + 1);
     const uint16_t* Ks = tile_buf(buf);
-    tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run,
-                                               (t_beg + it * SPLIT + grpk) * BC, N, wq_lo, a.sl2, lr, hh,
-                                               tr_row, tr_col);
+    tile_step<D, QW, BC, KP, VP, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, (t_beg + it * SPLIT + grpk) * BC, N,
+                                        wq_lo, a.sl2, lr, hh, tr_row, tr_col, false);
     if (it + 1 < nit) swrite(buf ^ 1);
     __syncthreads();
   }
@@ -456,12 +511,9 @@ void fwd_bf16_kernel(FwdArgs a) {
     const uint16_t* Ks = tile_buf(buf);
     const int t = it * SPLIT + grpk;
     const int key0 = (t_beg + t) * BC;
-    if (t < j_split)
-      tile_step<D, QW, BC, KP, VP, false, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, key0, N, wq_lo, a.sl2,
-                                                 lr, hh, tr_row, tr_col);
-    else if (t < nkv && (!CAUSAL || key0 <= wq_hi))
-      tile_step<D, QW, BC, KP, VP, true, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, key0, N, wq_lo, a.sl2,
-                                                lr, hh, tr_row, tr_col);
+    if (t < nkv && (!CAUSAL || key0 <= wq_hi))
+      tile_step<D, QW, BC, KP, VP, CAUSAL>(Ks, Ks + KT, qf, acc, m_run, l_run, key0, N, wq_lo, a.sl2, lr, hh,
+                                          tr_row, tr_col, t >= j_split);
     if (it + 1 < nit) swrite(buf ^ 1);
     __syncthreads();
   }
@@ -550,10 +602,10 @@ void fwd_bf16_kernel(FwdArgs a) {
           const int col = dt * 32 + 8 * g + 4 * hh;   // 4 consecutive features
           const float x0 = acc[qb][dt][4 * g + 0] * inv, x1 = acc[qb][dt][4 * g + 1] * inv;
           const float x2 = acc[qb][dt][4 * g + 2] * inv, x3 = acc[qb][dt][4 * g + 3] * inv;
-          if (FULLD) {
+          if (LD == LD_FULL || (LD == LD_VEC8 && col < d)) {
             const u32x2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
             *(u32x2*)(orow + col) = w;
-          } else {
+          } else if (LD == LD_ELEM) {
             const float xs[4] = {x0, x1, x2, x3};
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -569,18 +621,21 @@ void fwd_bf16_kernel(FwdArgs a) {
 }
 
 template <class C, bool CAUSAL, int SPLIT, bool PARTIAL>
-hipError_t launch_split(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
+hipError_t launch_split(const FwdArgs& a, int ld, int ncol, hipStream_t stream) {
   const dim3 grid((unsigned)(a.BH * a.n_qtiles), (unsigned)ncol);
   const dim3 block(C::NW * SPLIT * 64);
   // (head width exactly 128 runs on the tuned kernel in a single pass, so the generic 128-wide
   // kernel is built for full rows only where the split pass uses it)
   if constexpr (C::D != 128 || PARTIAL) {
-    if (fulld) {
-      hipLaunchKernelGGL((fwd_bf16_kernel<C, CAUSAL, true, SPLIT, PARTIAL>), grid, block, 0, stream, a);
+    if (ld == LD_FULL) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<C, CAUSAL, LD_FULL, SPLIT, PARTIAL>), grid, block, 0, stream, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((fwd_bf16_kernel<C, CAUSAL, false, SPLIT, PARTIAL>), grid, block, 0, stream, a);
+  if (ld == LD_VEC8)
+    hipLaunchKernelGGL((fwd_bf16_kernel<C, CAUSAL, LD_VEC8, SPLIT, PARTIAL>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<C, CAUSAL, LD_ELEM, SPLIT, PARTIAL>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -597,32 +652,32 @@ int choose_split(const FwdArgs& a, int keys, int ncol) {
 }
 
 template <class C, bool CAUSAL, bool PARTIAL>
-hipError_t launch_one(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
+hipError_t launch_one(const FwdArgs& a, int ld, int ncol, hipStream_t stream) {
   if constexpr (C::MAXSPLIT >= 4) {
     const int split = choose_split<C>(a, PARTIAL ? a.kv_chunk : a.N, ncol);
-    if (split == 4) return launch_split<C, CAUSAL, 4, PARTIAL>(a, fulld, ncol, stream);
-    if (split == 2) return launch_split<C, CAUSAL, 2, PARTIAL>(a, fulld, ncol, stream);
+    if (split == 4) return launch_split<C, CAUSAL, 4, PARTIAL>(a, ld, ncol, stream);
+    if (split == 2) return launch_split<C, CAUSAL, 2, PARTIAL>(a, ld, ncol, stream);
   }
-  return launch_split<C, CAUSAL, 1, PARTIAL>(a, fulld, ncol, stream);
+  return launch_split<C, CAUSAL, 1, PARTIAL>(a, ld, ncol, stream);
 }
 
 template <class C, bool PARTIAL>
-hipError_t launch_causal(const FwdArgs& a, bool fulld, bool causal, int ncol, hipStream_t stream) {
-  return causal ? launch_one<C, true, PARTIAL>(a, fulld, ncol, stream)
-                : launch_one<C, false, PARTIAL>(a, fulld, ncol, stream);
+hipError_t launch_causal(const FwdArgs& a, int ld, bool causal, int ncol, hipStream_t stream) {
+  return causal ? launch_one<C, true, PARTIAL>(a, ld, ncol, stream)
+                : launch_one<C, false, PARTIAL>(a, ld, ncol, stream);
 }
 
 // The split pass (PARTIAL) always runs the narrow configurations; the single pass at head
 // width 64 takes the wide blocks where d64_wide says so (its grid was sized for them).
 template <bool PARTIAL>
 hipError_t launch_generic(const FwdArgs& a, int d_pad, bool causal, int ncol, hipStream_t stream) {
-  const bool fulld = (a.d == d_pad);
+  const int ld = a.d == d_pad ? LD_FULL : (a.d % 8 == 0 ? LD_VEC8 : LD_ELEM);
   if (d_pad == 64) {
-    if (!PARTIAL && d64_wide(a.BH, a.N)) return launch_causal<CfgD64Wide, false>(a, fulld, causal, ncol, stream);
-    return launch_causal<Cfg<64>, PARTIAL>(a, fulld, causal, ncol, stream);
+    if (!PARTIAL && d64_wide(a.BH, a.N)) return launch_causal<CfgD64Wide, false>(a, ld, causal, ncol, stream);
+    return launch_causal<Cfg<64>, PARTIAL>(a, ld, causal, ncol, stream);
   }
-  if (d_pad == 128) return launch_causal<Cfg<128>, PARTIAL>(a, fulld, causal, ncol, stream);
-  return launch_causal<Cfg<256>, PARTIAL>(a, fulld, causal, ncol, stream);
+  if (d_pad == 128) return launch_causal<Cfg<128>, PARTIAL>(a, ld, causal, ncol, stream);
+  return launch_causal<Cfg<256>, PARTIAL>(a, ld, causal, ncol, stream);
 }
 
 }  // namespace

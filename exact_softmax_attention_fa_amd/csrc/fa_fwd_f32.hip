@@ -46,13 +46,15 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// 4 consecutive floats of one row, zero outside [0, d); the loads are unconditional (column
-// clamped) so that they issue together.
-__device__ __forceinline__ f32x4 load4_masked(const float* row, int col, int d) {
+// 4 consecutive floats of one row, zero outside [0, d). The row starts at element row0 of
+// base; elements are addressed by 32-bit indices off the uniform base (no 64-bit address per
+// element stays live). The loads are unconditional (column clamped) so that they issue
+// together.
+__device__ __forceinline__ f32x4 load4_masked(const float* base, uint32_t row0, int col, int d) {
   f32x4 r;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const float x = row[min(col + t, d - 1)];
+    const float x = base[row0 + (uint32_t)min(col + t, d - 1)];
     r[t] = (col + t < d) ? x : 0.0f;
   }
   return r;
@@ -110,7 +112,8 @@ void fwd_f32_kernel(FwdArgs a) {
   {
     const float sgn = a.neg ? -1.0f : 1.0f;
     const bool qv = qi < N;
-    const float* qrow = Qh + (size_t)min(qi, N - 1) * d;
+    const uint32_t qrow0 = (uint32_t)min(qi, N - 1) * (uint32_t)d;
+    const float* qrow = Qh + qrow0;
     if (FULLD) {
 #pragma unroll
       for (int v = 0; v < H2 / 4; ++v) {
@@ -122,7 +125,7 @@ void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < H2; ++kk) {
         const int col = kk + hh * H2;
-        const float x = qrow[min(col, d - 1)];
+        const float x = Qh[qrow0 + (uint32_t)min(col, d - 1)];
         qf[kk] = (qv && col < d) ? sgn * x : 0.0f;
       }
     }
@@ -160,12 +163,14 @@ void fwd_f32_kernel(FwdArgs a) {
       const int key = key0 + row;
       f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
       if (key < N) {
+        // one 32-bit element offset serves K and V (N * d < 2^31)
+        const uint32_t row0 = (uint32_t)key * (uint32_t)d;
         if (FULLD) {
-          kx = *(const f32x4*)(Kh + (size_t)key * d + col);
-          vx = *(const f32x4*)(Vh + (size_t)key * d + col);
+          kx = *(const f32x4*)(Kh + row0 + col);
+          vx = *(const f32x4*)(Vh + row0 + col);
         } else {
-          kx = load4_masked(Kh + (size_t)key * d, col, d);
-          vx = load4_masked(Vh + (size_t)key * d, col, d);
+          kx = load4_masked(Kh, row0, col, d);
+          vx = load4_masked(Vh, row0, col, d);
         }
       }
       kreg[r] = kx;
@@ -194,7 +199,11 @@ void fwd_f32_kernel(FwdArgs a) {
 
   for (int it = 0; it < nit; ++it) {
     const int buf = it & 1;
-    if (it + 1 < nit) gload(it + 1);
+    // The next step's tile is fetched into registers during this step's products, except at
+    // head widths above 128: there the 128 Q and 128 accumulator registers per lane leave no
+    // room for the staging registers beside the products, so the fetch follows them.
+    constexpr bool kOverlapFetch = D <= 128;
+    if (kOverlapFetch && it + 1 < nit) gload(it + 1);
     const float* Ks = smem + (buf * SPLIT + grpk) * (KT + VT);
     const float* Vs = Ks + KT;
     const int j = it * SPLIT + grpk;   // this key group's tile (relative to t_beg)
@@ -294,6 +303,7 @@ void fwd_f32_kernel(FwdArgs a) {
       }
     }
 
+    if (!kOverlapFetch && it + 1 < nit) gload(it + 1);
     if (it + 1 < nit) swrite(buf ^ 1);
     __syncthreads();
   }

@@ -23,7 +23,9 @@
  * attention does not mean bitwise equality").
  *
  * Layout: q, k, v, o are contiguous row-major [B][H][N][d] arrays (d fastest); lse is a
- * contiguous [B][H][N] fp32 array. All pointers are device pointers owned by the caller.
+ * contiguous [B][H][N] fp32 array. All pointers are device pointers owned by the caller;
+ * q, k, v, o (and the backward's dout, dq, dk, dv) must be 16-byte aligned and lse (and
+ * delta) 4-byte aligned, since rows are moved in 16-byte pieces.
  * The library allocates no device memory, keeps no state between calls and may be called
  * from several host threads at once.
  *
@@ -48,7 +50,8 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null q/k/v/o, B/H/N/d < 1, non-finite or non-positive-size problem,
-                              causal not 0/1, element count above 2^62 */
+                              causal not 0/1, element count above 2^62, misaligned or
+                              overlapping buffers */
   FA_ERR_UNSUPPORTED = -2, /* d > 256 (the largest head width compiled), or a grid too large */
   FA_ERR_HIP = -3,         /* the HIP runtime rejected the launch */
   FA_ERR_WORKSPACE = -4,   /* split-KV call: workspace missing or smaller than required */

@@ -106,6 +106,9 @@ int main() {
   expect("o overlaps q", fa_fwd(q, k, v, (char*)q + 64, lse, 1, 1, 16, 64, 0.125f, 0, nullptr), FA_ERR_INVALID_ARG);
   expect("lse overlaps o", fa_fwd(q, k, v, o, (float*)((char*)o + 8), 1, 1, 16, 64, 0.125f, 0, nullptr),
          FA_ERR_INVALID_ARG);
+  expect("q misaligned", fa_fwd((char*)q + 8, k, v, o, lse, 1, 1, 16, 64, 0.125f, 0, nullptr), FA_ERR_INVALID_ARG);
+  expect("lse misaligned", fa_fwd(q, k, v, o, (float*)((char*)lse + 2), 1, 1, 16, 64, 0.125f, 0, nullptr),
+         FA_ERR_INVALID_ARG);
   expect("splitkv small workspace",
          fa_fwd_splitkv(q, k, v, o, lse, 1, 1, 256, 64, 0.125f, 0, FA_F32, 8, (void*)(8 * G), 16, nullptr),
          FA_ERR_WORKSPACE);
@@ -132,7 +135,7 @@ int main() {
          FA_ERR_UNSUPPORTED);
   expect("bwd huge", fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, INT_MAX, INT_MAX, INT_MAX, 64, 0.1f, 0, nullptr),
          FA_ERR_INVALID_ARG);
-  expect("bwd dq overlaps dk", fa_bwd(q, k, v, o, dout, lse, dq, (char*)dq + 2, dv, delta, 1, 1, 16, 64, 0.1f, 0,
+  expect("bwd dq overlaps dk", fa_bwd(q, k, v, o, dout, lse, dq, (char*)dq + 16, dv, delta, 1, 1, 16, 64, 0.1f, 0,
                                       nullptr), FA_ERR_INVALID_ARG);
   for (int s = -3; s <= 6; ++s)
     if (fa_status_string(s) == nullptr) {

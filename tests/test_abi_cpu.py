@@ -80,6 +80,10 @@ def call(fn, q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=16, d=64, scale=0.125, causa
     (dict(o=Q + 64), fa.FA_ERR_INVALID_ARG),                                          # o overlaps q
     (dict(lse=V + 8), fa.FA_ERR_INVALID_ARG),                                         # lse overlaps v
     (dict(lse=O + 16), fa.FA_ERR_INVALID_ARG),                                        # lse overlaps o
+    (dict(q=Q + 8), fa.FA_ERR_INVALID_ARG),                                           # q not 16-byte aligned
+    (dict(v=V + 2), fa.FA_ERR_INVALID_ARG),                                           # v not 16-byte aligned
+    (dict(o=O + 4), fa.FA_ERR_INVALID_ARG),                                           # o not 16-byte aligned
+    (dict(lse=L + 2), fa.FA_ERR_INVALID_ARG),                                         # lse not 4-byte aligned
 ])
 def test_invalid_arguments_rejected_on_host(lib, fn, kwargs, status):
     assert call(fn, **kwargs) == status
@@ -105,9 +109,12 @@ def call_bwd(q=Q, k=K, v=V, o=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, delta=DL, 
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
     (dict(dq=Q + 64), fa.FA_ERR_INVALID_ARG),       # dq overlaps q
-    (dict(dk=DQ + 2), fa.FA_ERR_INVALID_ARG),       # dk overlaps dq
+    (dict(dk=DQ + 16), fa.FA_ERR_INVALID_ARG),      # dk overlaps dq
     (dict(delta=DO + 8), fa.FA_ERR_INVALID_ARG),    # workspace overlaps dout
-    (dict(dv=L + 4), fa.FA_ERR_INVALID_ARG),        # dv overlaps lse
+    (dict(dv=L + 16), fa.FA_ERR_INVALID_ARG),       # dv overlaps lse
+    (dict(dout=DO + 8), fa.FA_ERR_INVALID_ARG),     # dout not 16-byte aligned
+    (dict(dq=DQ + 4), fa.FA_ERR_INVALID_ARG),       # dq not 16-byte aligned
+    (dict(delta=DL + 2), fa.FA_ERR_INVALID_ARG),    # delta not 4-byte aligned
 ])
 def test_backward_invalid_arguments_rejected_on_host(lib, kwargs, status):
     assert call_bwd(**kwargs) == status

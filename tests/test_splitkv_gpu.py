@@ -45,7 +45,7 @@ def plan(t, dtype, causal, num_splits):
     return ns, wb
 
 
-@pytest.mark.parametrize("N,d", [(256, 64), (300, 128), (517, 96), (200, 256)])
+@pytest.mark.parametrize("N,d", [(256, 64), (300, 128), (517, 96), (200, 256), (301, 41), (150, 200)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("ns", [1, 2, 4, 8])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
