@@ -65,6 +65,10 @@ int validate(const void* q, const void* k, const void* v, void* o, float* lse,
   args->kv_chunk = N;
   args->part_u = nullptr;
   args->part_ml = nullptr;
+  // One-XCD packing for short sequences only: there it cuts the HBM traffic of the K/V
+  // re-reads at no cost in time, while long ones (all workgroups streaming K/V at once through
+  // one XCD) ran slower packed.
+  args->wg_shift = ((int64_t)B * H < 8 && (int64_t)B * H * n_qtiles <= 32 && N <= 1024) ? 3 : 0;
   *d_pad = dp;
   return FA_OK;
 }
@@ -155,6 +159,7 @@ int splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse
   }
   const int d_pad = plan.d_pad;
   args.kv_chunk = plan.kv_chunk;
+  args.wg_shift = 0;   // the split pass spreads its columns over the whole chip
   args.part_u = (float*)ws;
   args.part_ml = (float*)((uint8_t*)ws + ((plan.u_bytes + 255) / 256) * 256);
   const hipError_t e1 = bf ? fa::launch_bf16_partial(args, d_pad, causal != 0, plan.nsplit, stream)

@@ -364,7 +364,10 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   // Scheduler: heads vary fastest, so consecutive workgroups (which the dispatcher spreads
   // round-robin over the 8 XCDs) keep one head on one XCD whenever B*H is a multiple of 8.
-  const int id = blockIdx.x;
+  // (workgroups off the first XCD exit at once when the grid is packed onto one XCD; the
+  // exit is uniform over the workgroup and comes before any barrier)
+  if (blockIdx.x & ((1u << a.wg_shift) - 1u)) return;
+  const int id = (int)(blockIdx.x >> a.wg_shift);
   const int qt_rev = id / a.BH;
   const int bh = id - qt_rev * a.BH;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
@@ -622,7 +625,7 @@ void fwd_bf16_kernel(FwdArgs a) {
 
 template <class C, bool CAUSAL, int SPLIT, bool PARTIAL>
 hipError_t launch_split(const FwdArgs& a, int ld, int ncol, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.BH * a.n_qtiles), (unsigned)ncol);
+  const dim3 grid((unsigned)(a.BH * a.n_qtiles) << a.wg_shift, (unsigned)ncol);
   const dim3 block(C::NW * SPLIT * 64);
   // (head width exactly 128 runs on the tuned kernel in a single pass, so the generic 128-wide
   // kernel is built for full rows only where the split pass uses it)

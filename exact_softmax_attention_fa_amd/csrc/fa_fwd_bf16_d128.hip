@@ -137,7 +137,10 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   const int grp = wave >> 2;   // 0: runs ahead, 1: one phase behind
   const int N = a.N;
 
-  const int id = blockIdx.x;
+  // (workgroups off the first XCD exit at once when the grid is packed onto one XCD; the
+  // exit is uniform over the workgroup and comes before any barrier)
+  if (blockIdx.x & ((1u << a.wg_shift) - 1u)) return;
+  const int id = (int)(blockIdx.x >> a.wg_shift);
   const int qt_rev = id / a.BH;
   const int bh = id - qt_rev * a.BH;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
@@ -466,7 +469,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
 int bf16_d128_rows_per_block() { return BR; }
 
 hipError_t launch_bf16_d128(const FwdArgs& a, bool causal, hipStream_t stream) {
-  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3((unsigned)(a.BH * a.n_qtiles)), dim3(NT), 0, stream, a,
+  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3((unsigned)(a.BH * a.n_qtiles) << a.wg_shift), dim3(NT), 0, stream, a,
                      causal ? 1 : 0);
   return hipGetLastError();
 }

@@ -89,7 +89,10 @@ void fwd_f32_kernel(FwdArgs a) {
   const int lr = lane & 31, hh = lane >> 5;
   const int N = a.N, d = a.d;
 
-  const int id = blockIdx.x;
+  // (workgroups off the first XCD exit at once when the grid is packed onto one XCD; the
+  // exit is uniform over the workgroup and comes before any barrier)
+  if (blockIdx.x & ((1u << a.wg_shift) - 1u)) return;
+  const int id = (int)(blockIdx.x >> a.wg_shift);
   const int qt_rev = id / a.BH;
   const int bh = id - qt_rev * a.BH;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
@@ -390,7 +393,7 @@ void fwd_f32_kernel(FwdArgs a) {
 
 template <int D, bool CAUSAL, int SPLIT, bool PARTIAL>
 hipError_t launch_split(const FwdArgs& a, bool fulld, int ncol, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.BH * a.n_qtiles), (unsigned)ncol);
+  const dim3 grid((unsigned)(a.BH * a.n_qtiles) << a.wg_shift, (unsigned)ncol);
   const dim3 block(CfgF<D>::NW * SPLIT * 64);
   if (fulld) hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, true, SPLIT, PARTIAL>), grid, block, 0, stream, a);
   else       hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, false, SPLIT, PARTIAL>), grid, block, 0, stream, a);

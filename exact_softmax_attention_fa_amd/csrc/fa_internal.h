@@ -29,6 +29,11 @@ struct FwdArgs {
   int kv_chunk;
   float* part_u;
   float* part_ml;
+  // Single-pass grids of fewer than 8 short heads, small enough for one XCD (the dispatcher places
+  // workgroup i on XCD i mod 8) launch 2^wg_shift workgroups per work item along x and only
+  // those with blockIdx.x a multiple of 2^wg_shift work: every workgroup then runs on the
+  // same XCD and the heads' K/V come from HBM once into its L2, not once per XCD.
+  int wg_shift;
 };
 
 // Rows of queries per workgroup of the kernel that will run for head width d (host needs it

@@ -117,13 +117,39 @@ int main() {
          FA_ERR_INVALID_ARG);
   // launch arguments the front end computes
   expect("headline shape", fa_fwd(q, k, v, o, lse, 1, 16, 8192, 128, 0.088f, 0, nullptr), FA_OK);
-  if (g_last.BH != 16 || g_last.n_qtiles != 32 || g_last.N != 8192 || g_last.part_u != nullptr) {
-    fprintf(stderr, "FAIL headline launch arguments: BH=%d n_qtiles=%d\n", g_last.BH, g_last.n_qtiles);
+  if (g_last.BH != 16 || g_last.n_qtiles != 32 || g_last.N != 8192 || g_last.part_u != nullptr ||
+      g_last.wg_shift != 0) {
+    fprintf(stderr, "FAIL headline launch arguments: BH=%d n_qtiles=%d wg_shift=%d\n", g_last.BH, g_last.n_qtiles,
+            g_last.wg_shift);
+    ++g_fail;
+  }
+  // one head, 8 query tiles: packed onto one XCD (8 launched workgroups per work item)
+  expect("single head fp32", fa_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)o, lse, 1, 1,
+                                        256, 64, 0.125f, 0, nullptr), FA_OK);
+  if (g_last.n_qtiles != 8 || g_last.wg_shift != 3) {
+    fprintf(stderr, "FAIL single-head launch arguments: n_qtiles=%d wg_shift=%d\n", g_last.n_qtiles, g_last.wg_shift);
+    ++g_fail;
+  }
+  // 8 heads or more, or more than 32 workgroups: not packed
+  expect("eight heads", fa_fwd(q, k, v, o, lse, 2, 4, 256, 64, 0.125f, 0, nullptr), FA_OK);
+  if (g_last.wg_shift != 0) {
+    fprintf(stderr, "FAIL eight-head launch arguments: wg_shift=%d\n", g_last.wg_shift);
+    ++g_fail;
+  }
+  expect("one long head", fa_fwd(q, k, v, o, lse, 1, 1, 2048, 128, 0.088f, 0, nullptr), FA_OK);
+  if (g_last.n_qtiles != 8 || g_last.wg_shift != 0) {
+    fprintf(stderr, "FAIL long-head launch arguments: n_qtiles=%d wg_shift=%d\n", g_last.n_qtiles, g_last.wg_shift);
+    ++g_fail;
+  }
+  expect("one head, 64 tiles", fa_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)o, lse, 1, 1,
+                                          2048, 64, 0.125f, 0, nullptr), FA_OK);
+  if (g_last.wg_shift != 0) {
+    fprintf(stderr, "FAIL 64-tile launch arguments: wg_shift=%d\n", g_last.wg_shift);
     ++g_fail;
   }
   expect("split fp32 256", fa_fwd_splitkv(q, k, v, o, lse, 1, 1, 256, 64, 0.125f, 0, FA_F32, 8, (void*)(8 * G),
                                           1 << 30, nullptr), FA_OK);
-  if (g_last_ncol != 8 || g_last.kv_chunk != 32 || (uintptr_t)g_last.part_u != 8 * G) {
+  if (g_last_ncol != 8 || g_last.kv_chunk != 32 || (uintptr_t)g_last.part_u != 8 * G || g_last.wg_shift != 0) {
     fprintf(stderr, "FAIL split launch arguments: ncol=%d kv_chunk=%d\n", g_last_ncol, g_last.kv_chunk);
     ++g_fail;
   }
