@@ -39,14 +39,26 @@ CSRC = "exact_softmax_attention_fa_amd/csrc/"
 
 
 def kernel_sources(w: inputs.Workload) -> list:
-    """Sources of the kernel a workload runs (the key under which its traffic is stored)."""
+    """Sources of the kernel a workload runs (the key under which its traffic is stored): the
+    kernel, the headers it includes and the front end that computes its launch arguments."""
     if w.dtype == "f32":
-        main = "fa_fwd_f32.hip"
+        main = ["fa_fwd_f32.hip"]
     elif w.d == 128:
-        main = "fa_fwd_bf16_d128.hip"
+        main = ["fa_fwd_bf16_d128.hip", "fa_dma.h"]
     else:
-        main = "fa_fwd_bf16.hip"
-    return [CSRC + main, CSRC + "fa_internal.h"]
+        main = ["fa_fwd_bf16.hip"]
+    return [CSRC + m for m in main + ["fa_internal.h", "fa_api.hip"]]
+
+
+BACKWARD_SOURCES = [CSRC + m for m in ("fa_bwd_bf16.hip", "fa_bwd_internal.h", "fa_dma.h", "fa_api.hip")]
+
+
+def sources_hash(rels: list) -> str:
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
@@ -58,11 +70,7 @@ TRAFFIC = {
 
 
 def kernel_hash(w: inputs.Workload) -> str:
-    h = hashlib.sha256()
-    for rel in kernel_sources(w):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return sources_hash(kernel_sources(w))
 
 
 def library_info() -> dict:
@@ -222,7 +230,7 @@ def run_backward(w: inputs.Workload, q, k, v, o, lse, steps: int, warmup: int) -
     t = ev0.elapsed_time(ev1) / steps / 1e3
     flops = 2.5 * w.flops   # five N^2 d products per head against the forward's two
     return {"value": round(flops / t / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(t * 1e3, 4),
-            "algorithmic_flops_per_call": flops,
+            "algorithmic_flops_per_call": flops, "sources_hash": sources_hash(BACKWARD_SOURCES),
             "note": "flops counted as 2.5x the forward (S recomputed once); the kernels compute S and dP "
                     "twice (dK/dV pass and dQ pass), 3.5x the forward's products",
             "pct_of_peak": round(100.0 * flops / t / 1e12 / PEAK_TFLOPS[w.dtype], 2)}
