@@ -91,7 +91,7 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale when the max r
 #define FA_BF16_D128_WPE 2
 #endif
 #ifndef FA_BF16_D64W_NW
-#define FA_BF16_D64W_NW 8
+#define FA_BF16_D64W_NW 4
 #endif
 // Grids of at least this many workgroups of the wide head-width-64 configuration use it.
 #ifndef FA_BF16_D64W_MIN_WGS
@@ -105,9 +105,11 @@ template <> struct Cfg<64> {
   static constexpr int QW = FA_BF16_D64_QW, NW = FA_BF16_D64_NW, BC = FA_BF16_D64_BC, WPE = FA_BF16_D64_WPE;
   static constexpr int MAXSPLIT = 4;
 };
-// Head widths up to 64 on large grids: 8 waves share each K/V tile (four times fewer tile
-// loads per query than the 2-wave blocks), no key split. The 2-wave blocks with their key split
-// stay the choice for small grids, where the wide blocks would leave CUs idle.
+// Head widths up to 64 on large grids: 4 waves share each K/V tile (half the tile loads per
+// query of the 2-wave blocks), no key split; three such workgroups fit one CU (measured at
+// B1 H16 N8192 against 8 waves, of which only one workgroup fits: d64 865 against 851
+// TFLOP/s, d32 463 against 418). The 2-wave blocks with their key split stay the choice for
+// small grids, where the wide blocks would leave CUs idle.
 struct CfgD64Wide {
   static constexpr int D = 64;
   static constexpr int QW = 1, NW = FA_BF16_D64W_NW, BC = 64, WPE = 2;

@@ -21,7 +21,7 @@ int g_last_ncol = 0;
 // ---- stubs of the kernel side (same row and tile geometry as the kernels) -------------------
 namespace fa {
 int bf16_rows_per_block(int d, int64_t BH, int N) {
-  if (d <= 64) return BH * (((int64_t)N + 255) / 256) >= 256 ? 256 : 64;
+  if (d <= 64) return BH * (((int64_t)N + 127) / 128) >= 256 ? 128 : 64;
   return d == 128 ? 256 : (d <= 128 ? 256 : 128);
 }
 int f32_rows_per_block(int d) { return d <= 64 ? 32 : (d <= 128 ? 64 : 128); }

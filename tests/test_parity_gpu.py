@@ -227,8 +227,8 @@ def test_other_scales(dtype, scale):
 @pytest.mark.parametrize("B,H,N,d", [(4, 64, 256, 64), (2, 64, 300, 48), (1, 128, 513, 64), (2, 64, 257, 17)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_d64_wide_blocks(B, H, N, d, causal):
-    """Grids of at least 256 workgroups of 256 queries run the 8-wave blocks at head widths up
-    to 64 (many heads; ragged query and key tails, partial head widths, one and three query
+    """Grids of at least 256 workgroups of 128 queries run the 4-wave blocks at head widths up
+    to 64 (many heads; ragged query and key tails, partial head widths, two to five query
     tiles per head)."""
     t = inputs.make_random(B, H, N, d, "bf16", seed=1400 + N + d + H)
     full_parity(t, "bf16", 1 / math.sqrt(d), causal, f"bf16 wide B{B} H{H} N{N} d{d} causal={causal}")
@@ -237,6 +237,6 @@ def test_bf16_d64_wide_blocks(B, H, N, d, causal):
 @pytest.mark.parametrize("name", ["sweep_bf16_b1_h16_n8192_d32", "sweep_bf16_b1_h16_n8192_d64",
                                   "sweep_bf16_b1_h16_n8192_d96", "sweep_bf16_b1_h16_n8192_d256"])
 def test_head_width_sweep_sampled_rows(name):
-    """The other head widths at the headline's B, H and N (the 8-wave blocks at widths up to 64,
+    """The other head widths at the headline's B, H and N (the 4-wave blocks at widths up to 64,
     the generic 128- and 256-wide blocks above), on sampled rows of every head."""
     sampled_parity(inputs.ALL_WORKLOADS[name], 32, name)
