@@ -2,6 +2,11 @@
 
 Usage: ``python -m exact_softmax_attention_fa_amd.build`` (or ``build()`` from Python).
 Every call recompiles. The library lands next to this file, where the binding loads it.
+
+Timing variants: ``python -m exact_softmax_attention_fa_amd.build -D NAME=VALUE ... -o PATH`` builds
+the same sources with build-time tile macros (e.g. ``-D FA_BF16_D64W_NW=8``) into PATH instead of the
+product library; bench.py loads such a library through ``FA_LIBRARY=PATH`` and marks its line
+non-product.
 """
 from __future__ import annotations
 
@@ -34,8 +39,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build the HIP library)")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, extra_flags=(), output: str | None = None) -> str:
+    lib = os.path.abspath(output) if output else LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
@@ -47,9 +53,22 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def main(argv) -> None:
+    import argparse
+    ap = argparse.ArgumentParser(description="build libfa.so (or a timing variant) for gfx950")
+    ap.add_argument("-v", action="store_true", help="print the hipcc command and its messages")
+    ap.add_argument("-D", action="append", default=[], metavar="NAME=VALUE",
+                    help="build-time macro (tile configuration) for a timing variant")
+    ap.add_argument("-o", default=None, metavar="PATH", help="output library (default: the product library)")
+    args = ap.parse_args(argv)
+    if args.D and not args.o:
+        ap.error("a variant built with -D needs its own output path (-o)")
+    print(build(verbose=args.v, extra_flags=[f"-D{d}" for d in args.D], output=args.o))
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    main(sys.argv[1:])
