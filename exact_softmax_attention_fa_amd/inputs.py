@@ -114,6 +114,10 @@ EXTRA_WORKLOADS = {
     "fwd_bf16_b1_h1_n8192_d128_causal": Workload(
         "fwd_bf16_b1_h1_n8192_d128_causal", 1, 1, 8192, 128, "bf16", True, 1203,
         note="one head of the headline shape, bf16 N(0,1) inputs, causal"),
+    "fwd_bf16_b1_h16_n8192_d128_causal": Workload(
+        "fwd_bf16_b1_h16_n8192_d128_causal", 1, 16, 8192, 128, "bf16", True, 1204,
+        note="the headline shape under the causal mask, bf16 N(0,1) inputs (about the key tiles per CU "
+             "of B4 H16 N4096 causal, in half as many workgroups)"),
 }
 ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
 
