@@ -34,8 +34,18 @@
 //   reach 2^8, and l and u stay consistent because both use the same reference. The
 //   result is the same function; only the rounding differs.
 // * Causal: key tiles past the workgroup's last query are never loaded, a wave skips the
-//   tiles past its own last query, and only tiles that straddle the diagonal are masked.
-//   Workgroups are issued heaviest first.
+//   tiles past its own last query, and only tiles that straddle the diagonal (or the ragged
+//   end of the keys) are masked, by setting their dead scores to -inf before the update that
+//   every tile shares. Workgroups are issued heaviest first.
+// * Block shapes (Cfg): per padded head width, and at width 64 per grid size (4 waves with no
+//   key split on large grids, 2 waves with up to 4 key groups on small ones). A small grid
+//   splits the key range over key groups inside the workgroup, which merge their (m, l, u)
+//   through LDS at the end (interactiveml.org, merge of the three sufficient statistics).
+// * Row loads and stores (LD): whole 16-byte chunks at the full padded width; whole chunks or
+//   none when the width is a multiple of 8; element by element otherwise.
+// * PARTIAL instantiations run the split-KV partial pass: the workgroup covers one column of
+//   the key range (blockIdx.y) and writes its (m, l, u) to the caller's workspace for the
+//   merge kernel (fa_splitkv.hip) instead of o and lse.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -25,14 +25,15 @@ struct FwdArgs {
   // tile. With part_u == nullptr there is one column (kv_chunk >= N) and the kernel writes o
   // and lse; otherwise it writes its partial state (m, l, u) instead:
   //   part_u  [split][BH][N][d_pad] fp32: unnormalised numerator u
-  //   part_ml [split][BH][N][2]     fp32: reference m (see part_m_unscaled) and denominator l
+  //   part_ml [split][BH][N][2]     fp32: reference m (units: launch_merge's m_unscaled) and
+  //                                 denominator l
   int kv_chunk;
   float* part_u;
   float* part_ml;
-  // Single-pass grids of fewer than 8 short heads, small enough for one XCD (the dispatcher places
-  // workgroup i on XCD i mod 8) launch 2^wg_shift workgroups per work item along x and only
-  // those with blockIdx.x a multiple of 2^wg_shift work: every workgroup then runs on the
-  // same XCD and the heads' K/V come from HBM once into its L2, not once per XCD.
+  // Single-pass grids of fewer than 8 short heads, small enough for one XCD (the dispatcher
+  // places workgroup i on XCD i mod 8), launch 2^wg_shift workgroups per work item along x,
+  // and only those with blockIdx.x a multiple of 2^wg_shift work: every workgroup then runs on
+  // the same XCD and the heads' K/V come from HBM once into its L2, not once per XCD.
   int wg_shift;
 };
 

@@ -113,8 +113,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  *   dtype      : FA_BF16 (q, k, v, o bf16, as fa_fwd) or FA_F32 (fp32, as fa_fwd_f32)
  *   num_splits : 0 = the library's choice (one column when the single pass already has 256
  *                workgroups or more; else about 256 workgroups in all, 2048 under the causal
- *                mask), else 1..64 requested columns; the call uses at most one column per key tile of the kernel and
- *                drops columns that would hold no key (fa_fwd_splitkv_plan reports the count)
+ *                mask, in columns of at least 1024 keys), else 1..64 requested columns; the
+ *                call uses at most one column per key tile of the kernel and drops columns
+ *                that would hold no key (fa_fwd_splitkv_plan reports the count)
  *   workspace  : device memory owned by the caller, 256-byte aligned, at least the size
  *                fa_fwd_splitkv_plan reports for the same (B, H, N, d, dtype, causal,
  *                num_splits); its contents on entry are ignored and on return unspecified.
