@@ -318,13 +318,15 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
     s1 = c1;
   };
 
-  // O^T += V^T P^T from LDS slot VS (first PF steps already requested); its last steps request
-  // the first K operands of the S product that follows, from slot KS.
-  auto pv_product = [&](auto vs_tag, auto ks_tag) __attribute__((always_inline)) {
+  // O^T += V^T P^T from LDS slot VS (first PF steps already requested); unless it is the last
+  // product (KPF = 0), its last steps request the first K operands of the S product that
+  // follows, from slot KS.
+  auto pv_product = [&](auto vs_tag, auto ks_tag, auto kpf_tag) __attribute__((always_inline)) {
+    constexpr bool KPF = decltype(kpf_tag)::value != 0;
 #pragma unroll
     for (int st = 0; st < PV_STEPS; ++st) {
       if (st + PFV < PV_STEPS) v_load(st + PFV, vs_tag);
-      if (st + PF >= PV_STEPS) k_load(st + PF - PV_STEPS, ks_tag);
+      if (KPF && st + PF >= PV_STEPS) k_load(st + PF - PV_STEPS, ks_tag);
       __builtin_amdgcn_sched_barrier(0);
       const int c16 = st / (D / 32), dt = st % (D / 32);
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[st]),
@@ -336,17 +338,21 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // M phase of tile j held in LDS slot SLOT (j may equal nkv: then only the product with
   // V_{j-1} remains): first O^T += V_{j-1}^T P_{j-1}^T (its V operands were requested at the
   // end of the wave's previous V phase; V_{j-1} has been in LDS since before M_{j-1}), then
-  // S_j. Tile 0 (FIRST) has only S_0. The wave raises its issue priority so that the other
-  // wave's vector work on the same SIMD does not hold back its MFMA stream.
-  auto m_phase = [&](int j, auto slot_tag, auto first_tag) __attribute__((always_inline)) {
+  // S_j. Tile 0 (FIRST) has only S_0; the final M phase (LAST, j = nkv) only the product with
+  // V_{nkv-1}, and it reads nothing from the K ring. The wave raises its issue priority so that
+  // the other wave's vector work on the same SIMD does not hold back its MFMA stream.
+  auto m_phase = [&](int j, auto slot_tag, auto first_tag, auto last_tag) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot_tag)::value;
     constexpr bool FIRST = decltype(first_tag)::value != 0;
+    constexpr bool LAST = decltype(last_tag)::value != 0;
     __builtin_amdgcn_s_setprio(2);
     if constexpr (FIRST) {
       k_prefetch(IntC<SL>{});
       s_product(IntC<SL>{});
+    } else if constexpr (LAST) {
+      if (j - 1 <= j_last) pv_product(IntC<(SL + SLOTS - 1) % SLOTS>{}, IntC<SL>{}, IntC<0>{});
     } else if (j - 1 <= j_last) {   // otherwise j > j_last as well: nothing left for this wave
-      pv_product(IntC<(SL + SLOTS - 1) % SLOTS>{}, IntC<SL>{});
+      pv_product(IntC<(SL + SLOTS - 1) % SLOTS>{}, IntC<SL>{}, IntC<1>{});
       if (j < nkv && j <= j_last) s_product(IntC<SL>{});
     }
     __builtin_amdgcn_s_setprio(0);
@@ -417,7 +423,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   const int lag = grp;   // interval of this wave's M_0
   if (grp == 1) barrier_after(0);
   auto tile = [&](int j, auto slot_tag, auto first_tag) __attribute__((always_inline)) {
-    m_phase(j, slot_tag, first_tag);
+    m_phase(j, slot_tag, first_tag, IntC<0>{});
     barrier_after(2 * j + lag);
     if (j + 2 + grp < nkv) issue_tile(j + 2 + grp);
     v_phase(j, slot_tag);
@@ -436,32 +442,41 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   if (j < nkv) tile(j++, IntC<2>{}, IntC<0>{});
   if (j < nkv) tile(j++, IntC<3>{}, IntC<0>{});
   switch (nkv & (SLOTS - 1)) {   // the final M phase (product with V_{nkv-1} only)
-    case 0: m_phase(nkv, IntC<0>{}, IntC<0>{}); break;
-    case 1: m_phase(nkv, IntC<1>{}, IntC<0>{}); break;
-    case 2: m_phase(nkv, IntC<2>{}, IntC<0>{}); break;
-    default: m_phase(nkv, IntC<3>{}, IntC<0>{}); break;
+    case 0: m_phase(nkv, IntC<0>{}, IntC<0>{}, IntC<1>{}); break;
+    case 1: m_phase(nkv, IntC<1>{}, IntC<0>{}, IntC<1>{}); break;
+    case 2: m_phase(nkv, IntC<2>{}, IntC<0>{}, IntC<1>{}); break;
+    default: m_phase(nkv, IntC<3>{}, IntC<0>{}, IntC<1>{}); break;
   }
   if (grp == 0) barrier_after(2 * nkv);
   wait_vm<0>();
 
   // ---- epilogue: o = u / l, lse = (m + log2 l) * ln 2 -----------------------------------------
+  // A lane holds 4-feature pieces of one output row, so stores straight from the accumulators
+  // would touch 32 rows per instruction. The rows go out through LDS instead: after the last
+  // barrier nothing reads the K ring any more (the last S product ran before it, the final M
+  // phase reads only the V ring and no load is in flight), so each wave stages its 32 rows
+  // (8 KiB, bf16) in its own eighth of the K ring, 16-byte chunk c of row r at c ^ (r & 15),
+  // and reads them back as whole rows: each store writes 4 rows, 1 KiB contiguous.
   const float l_tot = pair_sum(l_run);
   const float inv = 1.0f / l_tot;
-  if (qi < N) {
-    uint16_t* orow = Oh + (size_t)qi * D;
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  const uint32_t stage = lds_base + (uint32_t)(wave * 32 * ROWB);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = dt * 32 + 8 * g + 4 * hh;
-        const u32x2 w = {pack_bf16x2(acc[dt][4 * g + 0] * inv, acc[dt][4 * g + 1] * inv),
-                         pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
-        *(u32x2*)(orow + col) = w;
-      }
-    if (a.lse != nullptr && hh == 0) {
-      a.lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+    for (int g = 0; g < 4; ++g) {   // features dt*32 + 8g + 4hh .. +3 = half hh of chunk 4dt + g
+      const u32x2 w = {pack_bf16x2(acc[dt][4 * g + 0] * inv, acc[dt][4 * g + 1] * inv),
+                       pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
+      const uint32_t chunk = (uint32_t)((4 * dt + g) ^ (lr & 15));
+      *(lds_u32x2*)(uintptr_t)(stage + (uint32_t)(lr * ROWB) + chunk * 16 + 8 * hh) = w;
     }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {   // lane l: row 4s + l/16, chunk l%16
+    const int r = 4 * s + (lane >> 4), c = lane & 15;
+    const u32x4 x = *(const lds_u32x4*)(uintptr_t)(stage + (uint32_t)(r * ROWB) + (uint32_t)((c ^ (r & 15)) * 16));
+    if (wq_lo + r < N) *(u32x4*)(Oh + (size_t)(wq_lo + r) * D + 8 * c) = x;
   }
+  if (a.lse != nullptr && hh == 0 && qi < N) a.lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
 }
 
 }  // namespace
