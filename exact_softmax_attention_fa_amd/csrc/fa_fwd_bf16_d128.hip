@@ -38,10 +38,16 @@
 // * A tile is masked only where it must be (the causal diagonal, the ragged last tile): the
 //   mask overwrites scores with -inf, the rest of the update is shared. Key rows past N are
 //   loaded from row N-1 (finite data, weight 0).
+// * The output rows leave through LDS (the K ring is idle after the last barrier of an item),
+//   so that every store writes whole rows.
+// * When there are more work items (query tile, head) than CUs, one workgroup per CU stays
+//   resident and runs a fixed sequence of items: no dispatch gap between items, and under the
+//   causal mask a balanced total per workgroup (see the schedule below).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <atomic>
 
 #include "fa_internal.h"
 #include "fa_dma.h"
@@ -133,14 +139,37 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
-  const int lr = lane & 31, hh = lane >> 5;
   const int grp = wave >> 2;   // 0: runs ahead, 1: one phase behind
   const int N = a.N;
 
   // (workgroups off the first XCD exit at once when the grid is packed onto one XCD; the
   // exit is uniform over the workgroup and comes before any barrier)
   if (blockIdx.x & ((1u << a.wg_shift) - 1u)) return;
-  const int id = (int)(blockIdx.x >> a.wg_shift);
+  // Work item id = qt_rev * BH + bh: query tile qt of head bh (heaviest causal tiles first,
+  // heads varying fastest). With at least one workgroup per item each workgroup takes one item.
+  // Otherwise the grid holds one workgroup per CU (a multiple of 8) and workgroup w, on XCD
+  // w % 8, runs the items id = w % 8 + 8k of that XCD, so that a head's K/V stay in one L2 as
+  // with one workgroup per item; k runs over the XCD's workgroups in rounds of alternating
+  // direction, so that under the causal mask the heaviest items of one round meet the
+  // lightest of the next. A workgroup that stays resident pays no dispatch gap between items.
+  const int nitems = a.BH * a.n_qtiles;
+  const bool persist = (int)(gridDim.x >> a.wg_shift) < nitems;
+  const int xcd = (int)(blockIdx.x & 7u), loc = (int)(blockIdx.x >> 3), nloc = (int)(gridDim.x >> 3);
+  const int nx = persist ? (nitems - xcd + 7) >> 3 : 1;
+  const int nrounds = persist ? (nx + nloc - 1) / nloc : 1;
+  for (int round = 0; round < nrounds; ++round) {
+  int id = (int)(blockIdx.x >> a.wg_shift);
+  if (persist) {
+    const int k = round * nloc + ((round & 1) ? nloc - 1 - loc : loc);
+    if (k >= nx) continue;
+    id = xcd + 8 * k;
+  }
+  // (per-lane addresses are formed anew for every item rather than kept live across items)
+  int lane_v = lane;
+  asm volatile("" : "+v"(lane_v));
+  const int lane = lane_v;
+  const int lr = lane & 31, hh = lane >> 5;
+
   const int qt_rev = id / a.BH;
   const int bh = id - qt_rev * a.BH;
   const int qt = CAUSAL ? (a.n_qtiles - 1 - qt_rev) : qt_rev;
@@ -477,15 +506,37 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
     if (wq_lo + r < N) *(u32x4*)(Oh + (size_t)(wq_lo + r) * D + 8 * c) = x;
   }
   if (a.lse != nullptr && hh == 0 && qi < N) a.lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+  // every wave has read its staged rows before the next item's loads refill the K ring
+  __syncthreads();
+  }
 }
 
 }  // namespace
 
 int bf16_d128_rows_per_block() { return BR; }
 
+// Workgroups of the kernel that stay resident at once on the current device: one per CU
+// (the kernel's LDS allows no second), rounded down to a multiple of 8 (XCDs); cached per device.
+static int resident_workgroups() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    n = cus & ~7;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_bf16_d128(const FwdArgs& a, bool causal, hipStream_t stream) {
-  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3((unsigned)(a.BH * a.n_qtiles) << a.wg_shift), dim3(NT), 0, stream, a,
-                     causal ? 1 : 0);
+  const int64_t nitems = (int64_t)a.BH * a.n_qtiles;
+  const int resident = resident_workgroups();
+  unsigned grid = (unsigned)(nitems << a.wg_shift);
+  if (a.wg_shift == 0 && resident >= 8 && nitems > resident) grid = (unsigned)resident;   // persistent
+  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(grid), dim3(NT), 0, stream, a, causal ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 from exact_softmax_attention_fa_amd import inputs
-from gpu_util import fp32_scaled_tolerance, full_parity, note, run_gpu, sampled_parity
+from gpu_util import compare, fp32_scaled_tolerance, full_parity, note, run_gpu, sampled_parity
+from oracle import attention as oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -240,3 +241,23 @@ def test_head_width_sweep_sampled_rows(name):
     """The other head widths at the headline's B, H and N (the 4-wave blocks at widths up to 64,
     the generic 128- and 256-wide blocks above), on sampled rows of every head."""
     sampled_parity(inputs.ALL_WORKLOADS[name], 32, name)
+
+
+@pytest.mark.parametrize("B,H,N", [(3, 40, 600), (2, 100, 300), (1, 130, 1000)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d128_more_items_than_cus(B, H, N, causal):
+    """d = 128 grids with more (query tile, head) items than CUs, where each workgroup stays
+    resident and runs a sequence of items; ragged N, so items of different lengths and ragged
+    last tiles follow each other in one workgroup. Oracle on sampled rows of every head."""
+    d = 128
+    label = f"bf16 B{B} H{H} N{N} d{d} causal={causal} ({B * H * -(-N // 256)} items)"
+    note(f"resident workgroups {label}")
+    t = inputs.make_random(B, H, N, d, "bf16", seed=7000 + B * 100 + H + N)
+    scale = 1 / math.sqrt(d)
+    o, l = run_gpu(t, "bf16", scale, causal)
+    rows = np.stack([np.stack([inputs.sample_rows(N, 16, seed=B * H * 10 + b * H + h)[:16] for h in range(H)])
+                     for b in range(B)])
+    o_ref, l_ref = oracle.attention_stored(t["q"], t["k"], t["v"], "bf16", scale, causal, rows=rows)
+    ib = np.arange(B)[:, None, None]
+    ih = np.arange(H)[None, :, None]
+    compare(o[ib, ih, rows], l[ib, ih, rows], o_ref, l_ref, "bf16", label)
