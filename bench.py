@@ -43,8 +43,8 @@ def kernel_sources(w: inputs.Workload) -> list:
     kernel, the headers it includes and the front end that computes its launch arguments."""
     if w.dtype == "f32":
         main = ["fa_fwd_f32.hip"]
-    elif w.d == 128:
-        main = ["fa_fwd_bf16_d128.hip", "fa_dma.h"]
+    elif w.d == 128 or (w.d == 64 and w.B * w.H * -(-w.N // 256) >= 256):   # the tuned kernels
+        main = ["fa_fwd_bf16_tuned.hip", "fa_dma.h"]
     else:
         main = ["fa_fwd_bf16.hip"]
     return [CSRC + m for m in main + ["fa_internal.h", "fa_api.hip"]]

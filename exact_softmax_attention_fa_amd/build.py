@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_bf16_d128.hip", "fa_fwd_f32.hip", "fa_splitkv.hip",
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_bf16_tuned.hip", "fa_fwd_f32.hip", "fa_splitkv.hip",
            "fa_noalloc.hip", "fa_bwd_bf16.hip"]
 
 HIPCC_FLAGS = [

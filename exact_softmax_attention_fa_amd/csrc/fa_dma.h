@@ -30,19 +30,35 @@ FA_HD uint32_t past_end_back(int row0, int r, int N, int row_bytes) {
   return over > 0 ? (uint32_t)over * (uint32_t)row_bytes : 0u;
 }
 
-// ---- forward kernel for head width 128: 64-key tiles of K and V, 8 waves --------------------
-// Wave w's load instruction i (0 or 1) fills LDS bytes [(2w+i) KiB, +1 KiB) of the tile: lane l
-// takes row 4(2w+i) + l/16 and physical chunk l%16, i.e. K chunk (l%16) ^ (row & 15) or V
-// chunk (l%16) ^ 4(row & 3) of that row.
-constexpr int kFwd128RowBytes = 128 * 2;
-FA_HD int fwd128_row(int wave, int lane, int i) { return (2 * wave + i) * 4 + (lane >> 4); }
-FA_HD uint32_t fwd128_k_off(int wave, int lane, int i) {
-  const int r = fwd128_row(wave, lane, i);
-  return (uint32_t)(r * kFwd128RowBytes + ((lane & 15) ^ (r & 15)) * 16);
+// ---- tuned forward kernels, head width D = 64 or 128: 64-key tiles of K and V, 8 waves ------
+// A tile is 64 rows of 2D bytes, D/8 chunks of 16 bytes per row. Wave w's load instruction i
+// (0 <= i < D/64) fills LDS bytes [((D/64) w + i) KiB, +1 KiB) of the tile: lane l takes row
+// ((D/64) w + i) (512/D) + l/(D/8) and physical chunk l%(D/8), i.e. the logical K chunk
+// (l%(D/8)) ^ fwd_k_swz(row) or V chunk (l%(D/8)) ^ fwd_v_swz(row) of that row.
+// The K permutation makes the 16-byte operand reads of 16 consecutive rows hit distinct banks
+// (D = 128: 256-byte rows, chunk ^ (r & 15); D = 64: 128-byte rows, pairs of rows share a bank
+// row, chunk ^ ((r >> 1) & 7)); the V permutation does the same for the transpose reads of 4
+// consecutive rows and two 16-feature halves (4(r & 3), or 4((r >> 1) & 1) for D = 64). Both are
+// periodic in 16 rows, so row offsets of 16 and 32 keep them.
+template <int D> constexpr int fwd_row_bytes() { return 2 * D; }
+template <int D>
+FA_HD int fwd_k_swz(int r) {
+  static_assert(D == 64 || D == 128, "head width");
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
-FA_HD uint32_t fwd128_v_off(int wave, int lane, int i) {
-  const int r = fwd128_row(wave, lane, i);
-  return (uint32_t)(r * kFwd128RowBytes + ((lane & 15) ^ ((r & 3) << 2)) * 16);
+template <int D>
+FA_HD int fwd_v_swz(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+template <int D>
+FA_HD int fwd_row(int wave, int lane, int i) { return ((D / 64) * wave + i) * (512 / D) + lane / (D / 8); }
+template <int D>
+FA_HD uint32_t fwd_k_off(int wave, int lane, int i) {
+  const int r = fwd_row<D>(wave, lane, i);
+  return (uint32_t)(r * fwd_row_bytes<D>() + ((lane % (D / 8)) ^ fwd_k_swz<D>(r)) * 16);
+}
+template <int D>
+FA_HD uint32_t fwd_v_off(int wave, int lane, int i) {
+  const int r = fwd_row<D>(wave, lane, i);
+  return (uint32_t)(r * fwd_row_bytes<D>() + ((lane % (D / 8)) ^ fwd_v_swz<D>(r)) * 16);
 }
 
 // ---- backward kernels: [32][D] tiles, 16-byte chunk L of row r stored at L ^ swz(r) --------

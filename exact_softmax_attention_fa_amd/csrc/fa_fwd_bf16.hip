@@ -698,14 +698,14 @@ hipError_t launch_generic(const FwdArgs& a, int d_pad, bool causal, int ncol, hi
 }  // namespace
 
 int bf16_rows_per_block(int d, int64_t BH, int N) {
-  if (d == 128) return bf16_d128_rows_per_block();
+  if (d == 128 || (d == 64 && bf16_tuned_d64(BH, N))) return bf16_tuned_rows_per_block();
   if (d <= 64) return d64_wide(BH, N) ? CfgD64Wide::NW * CfgD64Wide::QW * 32 : Cfg<64>::NW * Cfg<64>::QW * 32;
   if (d <= 128) return Cfg<128>::NW * Cfg<128>::QW * 32;
   return Cfg<256>::NW * Cfg<256>::QW * 32;
 }
 
 hipError_t launch_bf16(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream) {
-  if (a.d == 128) return launch_bf16_d128(a, causal, stream);
+  if (a.d == 128 || (a.d == 64 && bf16_tuned_d64(a.BH, a.N))) return launch_bf16_tuned(a, causal, stream);
   return launch_generic<false>(a, d_pad, causal, 1, stream);
 }
 

@@ -1,5 +1,5 @@
-// Fused forward pass of exact softmax attention, bf16, head width exactly 128: the tuned
-// gfx950 kernel for long sequences.
+// Fused forward pass of exact softmax attention, bf16, head width exactly 128 or exactly 64:
+// the tuned gfx950 kernels for long sequences (one body, instantiated for each width).
 //
 // Same arithmetic as the generic bf16 kernel (online softmax over key tiles: running max,
 // denominator and unnormalised numerator rescaled together when the max rises; liminalml.com
@@ -13,14 +13,14 @@
 //   separated by workgroup barriers. While one group is in an M phase the other is in a V
 //   phase, so each SIMD keeps its matrix unit busy with one wave while the other wave's
 //   vector work runs alongside.
-// * K and V tiles (64 keys x 128 features) go from HBM straight into LDS with
+// * K and V tiles (64 keys x D features) go from HBM straight into LDS with
 //   global_load_lds_dwordx4 (no staging registers, no LDS write instructions) into rings of
 //   4 slots, requested at the start of V phases (two tiles ahead for the leading group, three
 //   for the other), where the vector work leaves issue slack. Each wave's load instruction fills
 //   1 KiB of LDS (lane l -> byte 16*l), so rows are stored unpadded and the 16-byte chunks of
-//   each row are XOR-swizzled: K chunk c of row r sits at c ^ (r & 15) (the 16-byte operand
-//   reads of 16 consecutive rows hit distinct banks), V chunk c at c ^ 4*(r & 3) (the
-//   transpose reads of 4 consecutive rows and two 16-feature halves hit distinct banks).
+//   each row are XOR-swizzled so that the 16-byte K operand reads of 16 consecutive rows, and
+//   the V transpose reads of 4 consecutive rows and two 16-feature halves, hit distinct banks
+//   (the permutations are in fa_dma.h).
 // * Operand reads from LDS run a few MFMAs ahead. The first V^T operands of M_j are requested
 //   at the end of the wave's V_{j-1} phase (V_{j-1} has been in LDS since M_{j-1}) and the first
 //   K operands of S_j during the last steps of the V product, so that neither product of an M
@@ -40,8 +40,8 @@
 //   loaded from row N-1 (finite data, weight 0).
 // * The output rows leave through LDS (the K ring is idle after the last barrier of an item),
 //   so that every store writes whole rows.
-// * When there are more work items (query tile, head) than CUs, one workgroup per CU stays
-//   resident and runs a fixed sequence of items: no dispatch gap between items, and under the
+// * When there are more work items (query tile, head) than workgroups that fit on the chip at
+//   once, that many stay resident and each runs a fixed sequence of items: no dispatch gap between items, and under the
 //   causal mask a balanced total per workgroup (see the schedule below).
 
 #include <hip/hip_runtime.h>
@@ -66,17 +66,21 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int D = 128;          // head width
 constexpr int BC = 64;          // keys per tile
 constexpr int NW = 8;           // waves per workgroup
 constexpr int NT = NW * 64;
 constexpr int BR = NW * 32;     // query rows per workgroup
-constexpr int ROWB = D * 2;     // bytes per key row in LDS
-constexpr int TILEB = BC * ROWB;  // 16 KiB per K or V tile
 constexpr int SLOTS = 4;
-constexpr int VREGION = SLOTS * TILEB;          // V ring starts after the K ring (64 KiB)
-constexpr int LDS_BYTES = 2 * SLOTS * TILEB;    // 128 KiB
-constexpr int LOADS_PER_TILE = 2 * (TILEB / 16) / NT;  // DMA instructions per thread per tile (K + V) = 4
+// Per head width D: bytes per key row in LDS, per K or V tile (16 KiB at D = 128, 8 KiB at 64),
+// the V ring's start after the K ring, the rings' LDS (128 or 64 KiB), and the DMA instructions
+// each thread issues per tile (K + V: 4 or 2).
+template <int D> struct Tiles {
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILEB = BC * ROWB;
+  static constexpr int VREGION = SLOTS * TILEB;
+  static constexpr int LDS_BYTES = 2 * SLOTS * TILEB;
+  static constexpr int LOADS_PER_TILE = 2 * (TILEB / 16) / NT;
+};
 // A tile whose per-lane probability sum exceeds 2^64 raises the reference (see v_phase).
 constexpr float kRaiseSum = 18446744073709551616.0f;   // 2^64
 // Reference before the first tile: finite (so that masked scores give exp2(-inf) = 0, never
@@ -124,6 +128,7 @@ __device__ __forceinline__ void wait_vm() {
 // wave's next M phase from a slot that no load overwrites before that phase has ended. The
 // compiler does not see the LDS writes of the DMA loads, so the barrier is also a compiler
 // memory barrier.
+template <int LOADS_PER_TILE>
 __device__ __forceinline__ void phase_barrier(int ahead) {
   if (ahead >= 2) wait_vm<2 * LOADS_PER_TILE, 15>();
   else if (ahead == 1) wait_vm<LOADS_PER_TILE, 15>();
@@ -131,8 +136,11 @@ __device__ __forceinline__ void phase_barrier(int ahead) {
   asm volatile("s_barrier" ::: "memory");
 }
 
-__global__ __launch_bounds__(NT, 2)
-void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
+template <int D>
+__device__ __forceinline__ void fwd_tuned_body(FwdArgs a, int causal_flag) {
+  static_assert(D == 64 || D == 128, "head width");
+  constexpr int ROWB = Tiles<D>::ROWB, TILEB = Tiles<D>::TILEB, VREGION = Tiles<D>::VREGION;
+  constexpr int LDS_BYTES = Tiles<D>::LDS_BYTES, LOADS_PER_TILE = Tiles<D>::LOADS_PER_TILE;
   const bool CAUSAL = causal_flag != 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
@@ -147,7 +155,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   if (blockIdx.x & ((1u << a.wg_shift) - 1u)) return;
   // Work item id = qt_rev * BH + bh: query tile qt of head bh (heaviest causal tiles first,
   // heads varying fastest). With at least one workgroup per item each workgroup takes one item.
-  // Otherwise the grid holds one workgroup per CU (a multiple of 8) and workgroup w, on XCD
+  // Otherwise the grid holds the workgroups that fit at once (a multiple of 8) and workgroup w, on XCD
   // w % 8, runs the items id = w % 8 + 8k of that XCD, so that a head's K/V stay in one L2 as
   // with one workgroup per item; k runs over the XCD's workgroups in rounds of alternating
   // direction, so that under the causal mask the heaviest items of one round meet the
@@ -203,23 +211,25 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   const int j_last = CAUSAL ? min(nkv - 1, wq_hi / BC) : nkv - 1;   // last tile this wave uses
 
   // ---- LDS DMA addressing ----------------------------------------------------------------
-  // Each thread issues 2 K and 2 V load instructions per tile. For instruction i the wave
-  // fills LDS bytes [(2*wave+i)*1024, +1024) of the slot; lane l writes physical chunk l%16
-  // of row (2*wave+i)*4 + l/16 and so fetches the logical chunk the swizzle places there.
+  // Each thread issues D/64 K and D/64 V load instructions per tile. For instruction i the wave
+  // fills LDS bytes [((D/64)*wave+i)*1024, +1024) of the slot; lane l writes physical chunk
+  // l%(D/8) of row ((D/64)*wave+i)*(512/D) + l/(D/8) and so fetches the logical chunk the
+  // swizzle places there.
   // The per-lane byte offsets inside a tile are fixed; the tile's base address advances in
   // scalar registers, so issuing a whole tile costs no vector instructions.
-  static_assert(dma::kFwd128RowBytes == ROWB, "row size of the load arithmetic");
-  uint32_t gk_off[2], gv_off[2];
-  int dma_row[2];
+  static_assert(dma::fwd_row_bytes<D>() == ROWB, "row size of the load arithmetic");
+  constexpr int NLD = D / 64;   // load instructions per thread for each of K and V
+  uint32_t gk_off[NLD], gv_off[NLD];
+  int dma_row[NLD];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    dma_row[i] = dma::fwd128_row(wave, lane, i);
-    gk_off[i] = dma::fwd128_k_off(wave, lane, i);
-    gv_off[i] = dma::fwd128_v_off(wave, lane, i);
+  for (int i = 0; i < NLD; ++i) {
+    dma_row[i] = dma::fwd_row<D>(wave, lane, i);
+    gk_off[i] = dma::fwd_k_off<D>(wave, lane, i);
+    gv_off[i] = dma::fwd_v_off<D>(wave, lane, i);
   }
   // LDS byte address of the buffer (address-space cast, then the 32-bit LDS offset)
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
-  const uint32_t dma_lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_base + (uint32_t)(2 * wave * 1024)));
+  const uint32_t dma_lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_base + (uint32_t)(NLD * wave * 1024)));
   int last_issued = -1;
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
     last_issued = t;
@@ -229,14 +239,14 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
     const uint8_t* vt = Vb + (size_t)key0 * ROWB;
     if (key0 + BC <= N) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < NLD; ++i) {
         const uint32_t ldst = dma_lds + slot + (uint32_t)(i * 1024);
         dma16(kt, gk_off[i], ldst);
         dma16(vt, gv_off[i], ldst + VREGION);
       }
     } else {   // ragged last tile: rows past the end read row N-1 instead (weight 0 later)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < NLD; ++i) {
         const uint32_t back = dma::past_end_back(key0, dma_row[i], N, ROWB);
         const uint32_t ldst = dma_lds + slot + (uint32_t)(i * 1024);
         dma16(kt, gk_off[i] - back, ldst);
@@ -251,7 +261,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   uint32_t koff[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    koff[kk] = lds_base + (uint32_t)(lr * ROWB + (((2 * kk + hh) ^ (lr & 15)) * 16));
+    koff[kk] = lds_base + (uint32_t)(lr * ROWB + (((2 * kk + hh) ^ dma::fwd_k_swz<D>(lr)) * 16));
   // V transpose reads: in each 16-lane group, lane 4r+q reads key row r (+8 for the second
   // read) at features 4q..4q+3 of the 16-wide half b of 32-feature block dt.
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
@@ -259,7 +269,7 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   uint32_t voff[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
-    const int chunk = (4 * dt + 2 * b16 + ((lane & 3) >> 1)) ^ ((tr_row & 3) << 2);
+    const int chunk = (4 * dt + 2 * b16 + ((lane & 3) >> 1)) ^ dma::fwd_v_swz<D>(tr_row);
     voff[dt] = lds_base + VREGION + (uint32_t)(tr_row * ROWB + chunk * 16 + 8 * (lane & 1));
   }
 
@@ -281,13 +291,15 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // 0 requests tile j+2 in V_j (interval 2j+1), group 1 tile j+3 in its V_j (interval 2j+2).
   // Tile t goes to the slot of tile t-4, whose last readers (the V products of M_{t-3}) ran in
   // intervals 2t-6 and 2t-5, before either request.
-  auto barrier_after = [&](int k) __attribute__((always_inline)) { phase_barrier(last_issued - ((k + 1) >> 1)); };
+  auto barrier_after = [&](int k) __attribute__((always_inline)) {
+    phase_barrier<LOADS_PER_TILE>(last_issued - ((k + 1) >> 1));
+  };
 
   // prologue: every wave requests its share of tiles 0 and 1; tile 0 lands before interval 0
   issue_tile(0);
   if (nkv > 1) issue_tile(1);
   if (grp == 1 && nkv > 2) issue_tile(2);
-  phase_barrier(last_issued);
+  phase_barrier<LOADS_PER_TILE>(last_issued);
 
   // Operand reads run PF steps ahead of the MFMAs; scheduling barriers keep the compiler from
   // sinking them next to their uses. The reads of one product's first PF steps are issued
@@ -484,11 +496,14 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   // would touch 32 rows per instruction. The rows go out through LDS instead: after the last
   // barrier nothing reads the K ring any more (the last S product ran before it, the final M
   // phase reads only the V ring and no load is in flight), so each wave stages its 32 rows
-  // (8 KiB, bf16) in its own eighth of the K ring, 16-byte chunk c of row r at c ^ (r & 15),
-  // and reads them back as whole rows: each store writes 4 rows, 1 KiB contiguous.
+  // (64 D bytes, bf16) in its own eighth of the K ring, 16-byte chunk c of row r at
+  // c ^ (r mod D/8), and reads them back as whole rows: each store writes 1 KiB contiguous
+  // (512/D rows).
   const float l_tot = pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPS = 1024 / ROWB;    // rows per 1 KiB store
   const uint32_t stage = lds_base + (uint32_t)(wave * 32 * ROWB);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -496,13 +511,13 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
     for (int g = 0; g < 4; ++g) {   // features dt*32 + 8g + 4hh .. +3 = half hh of chunk 4dt + g
       const u32x2 w = {pack_bf16x2(acc[dt][4 * g + 0] * inv, acc[dt][4 * g + 1] * inv),
                        pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
-      const uint32_t chunk = (uint32_t)((4 * dt + g) ^ (lr & 15));
+      const uint32_t chunk = (uint32_t)((4 * dt + g) ^ (lr & (CPR - 1)));
       *(lds_u32x2*)(uintptr_t)(stage + (uint32_t)(lr * ROWB) + chunk * 16 + 8 * hh) = w;
     }
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {   // lane l: row 4s + l/16, chunk l%16
-    const int r = 4 * s + (lane >> 4), c = lane & 15;
-    const u32x4 x = *(const lds_u32x4*)(uintptr_t)(stage + (uint32_t)(r * ROWB) + (uint32_t)((c ^ (r & 15)) * 16));
+  for (int s = 0; s < 32 / RPS; ++s) {   // lane l: row RPS s + l/CPR, chunk l%CPR
+    const int r = RPS * s + lane / CPR, c = lane % CPR;
+    const u32x4 x = *(const lds_u32x4*)(uintptr_t)(stage + (uint32_t)(r * ROWB) + (uint32_t)((c ^ (r & (CPR - 1))) * 16));
     if (wq_lo + r < N) *(u32x4*)(Oh + (size_t)(wq_lo + r) * D + 8 * c) = x;
   }
   if (a.lse != nullptr && hh == 0 && qi < N) a.lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
@@ -511,33 +526,51 @@ void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) {
   }
 }
 
-}  // namespace
+__global__ __launch_bounds__(NT, 2)
+void fwd_bf16_d128_kernel(FwdArgs a, int causal_flag) { fwd_tuned_body<128>(a, causal_flag); }
 
-int bf16_d128_rows_per_block() { return BR; }
+__global__ __launch_bounds__(NT, 2)
+void fwd_bf16_d64_kernel(FwdArgs a, int causal_flag) { fwd_tuned_body<64>(a, causal_flag); }
 
-// Workgroups of the kernel that stay resident at once on the current device: one per CU
-// (the kernel's LDS allows no second), rounded down to a multiple of 8 (XCDs); cached per device.
-static int resident_workgroups() {
+// Workgroups of a kernel that stay resident at once on the current device (CUs times the
+// kernel's workgroups per CU), rounded down to a multiple of 8 (XCDs); cached per device.
+template <int D>
+int resident_workgroups() {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   int n = cache[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    int cus = 0;
+    int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    n = cus & ~7;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, D == 128 ? fwd_bf16_d128_kernel : fwd_bf16_d64_kernel,
+                                                     NT, 0) != hipSuccess || per_cu < 1)
+      return 0;
+    n = (cus * per_cu) & ~7;
     cache[dev].store(n, std::memory_order_relaxed);
   }
   return n;
 }
 
-hipError_t launch_bf16_d128(const FwdArgs& a, bool causal, hipStream_t stream) {
+template <int D>
+hipError_t launch_tuned(const FwdArgs& a, bool causal, hipStream_t stream) {
   const int64_t nitems = (int64_t)a.BH * a.n_qtiles;
-  const int resident = resident_workgroups();
+  const int resident = resident_workgroups<D>();
   unsigned grid = (unsigned)(nitems << a.wg_shift);
   if (a.wg_shift == 0 && resident >= 8 && nitems > resident) grid = (unsigned)resident;   // persistent
-  hipLaunchKernelGGL(fwd_bf16_d128_kernel, dim3(grid), dim3(NT), 0, stream, a, causal ? 1 : 0);
+  hipLaunchKernelGGL(D == 128 ? fwd_bf16_d128_kernel : fwd_bf16_d64_kernel, dim3(grid), dim3(NT), 0, stream, a,
+                     causal ? 1 : 0);
   return hipGetLastError();
+}
+
+}  // namespace
+
+int bf16_tuned_rows_per_block() { return BR; }
+
+bool bf16_tuned_d64(int64_t BH, int N) { return BH * (((int64_t)N + BR - 1) / BR) >= 256; }
+
+hipError_t launch_bf16_tuned(const FwdArgs& a, bool causal, hipStream_t stream) {
+  return a.d == 128 ? launch_tuned<128>(a, causal, stream) : launch_tuned<64>(a, causal, stream);
 }
 
 }  // namespace fa

@@ -48,9 +48,12 @@ int f32_rows_per_block(int d);
 hipError_t launch_bf16(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream);
 hipError_t launch_f32(const FwdArgs& a, int d_pad, bool causal, hipStream_t stream);
 
-// Tuned bf16 kernel for head width exactly 128 (rows per workgroup, launch).
-int bf16_d128_rows_per_block();
-hipError_t launch_bf16_d128(const FwdArgs& a, bool causal, hipStream_t stream);
+// Tuned bf16 kernels for head width exactly 128 or 64 (a.d): rows per workgroup, whether a grid
+// of BH heads of N queries at d = 64 takes the tuned kernel (enough work items for the chip),
+// and the launch.
+int bf16_tuned_rows_per_block();
+bool bf16_tuned_d64(int64_t BH, int N);
+hipError_t launch_bf16_tuned(const FwdArgs& a, bool causal, hipStream_t stream);
 
 // ---- key-range split (split-KV) -------------------------------------------------------------
 // Rows per workgroup and keys per tile of the generic kernel that runs the partial pass

@@ -21,11 +21,11 @@ int g_last_ncol = 0;
 // ---- stubs of the kernel side (same row and tile geometry as the kernels) -------------------
 namespace fa {
 int bf16_rows_per_block(int d, int64_t BH, int N) {
+  if (d == 64 && BH * (((int64_t)N + 255) / 256) >= 256) return 256;   // tuned kernel
   if (d <= 64) return BH * (((int64_t)N + 127) / 128) >= 256 ? 128 : 64;
   return d == 128 ? 256 : (d <= 128 ? 256 : 128);
 }
 int f32_rows_per_block(int d) { return d <= 64 ? 32 : (d <= 128 ? 64 : 128); }
-int bf16_d128_rows_per_block() { return 256; }
 int bf16_split_rows_per_block(int d_pad) { return d_pad <= 64 ? 64 : (d_pad <= 128 ? 256 : 128); }
 int bf16_split_key_tile(int d_pad) { return d_pad <= 128 ? 64 : 32; }
 int f32_split_key_tile(int) { return 32; }
@@ -38,7 +38,6 @@ static hipError_t record(const FwdArgs& a, int ncol) {
 }
 hipError_t launch_bf16(const FwdArgs& a, int, bool, hipStream_t) { return record(a, 1); }
 hipError_t launch_f32(const FwdArgs& a, int, bool, hipStream_t) { return record(a, 1); }
-hipError_t launch_bf16_d128(const FwdArgs& a, bool, hipStream_t) { return record(a, 1); }
 hipError_t launch_bf16_partial(const FwdArgs& a, int, bool, int ns, hipStream_t) { return record(a, ns); }
 hipError_t launch_f32_partial(const FwdArgs& a, int, bool, int ns, hipStream_t) { return record(a, ns); }
 hipError_t launch_merge(const FwdArgs& a, int, bool, int ns, bool, bool, hipStream_t) { return record(a, ns); }

@@ -47,10 +47,14 @@ static void check_load(const char* k, int N, int D, int row_bytes, int64_t base,
   if (src != want) bad("reads the wrong row or chunk", k, N, D, a, b, c, src - want);
 }
 
-// ---- forward, head width 128 ---------------------------------------------------------------
-static void fwd128(int N, bool causal) {
-  const int BR = 256, BC = 64, SLOTS = 4, ROWB = kFwd128RowBytes, TILEB = BC * ROWB;
-  const int VREGION = SLOTS * TILEB, LDS = 2 * SLOTS * TILEB;
+// ---- forward, tuned kernels (head width D = 128 or 64) ---------------------------------------
+// The expected chunks restate the permutations: D = 128 K c ^ (r & 15), V c ^ 4(r & 3);
+// D = 64 K c ^ ((r >> 1) & 7), V c ^ 4((r >> 1) & 1).
+template <int D>
+static void fwd(int N, bool causal) {
+  const int BR = 256, BC = 64, SLOTS = 4, ROWB = fwd_row_bytes<D>(), TILEB = BC * ROWB;
+  const int VREGION = SLOTS * TILEB, LDS = 2 * SLOTS * TILEB, CPR = D / 8, NLD = D / 64;
+  const char* kn = D == 128 ? "fwd128" : "fwd64";
   const int nqt = (N + BR - 1) / BR;
   for (int qt = 0; qt < nqt; ++qt) {
     const int kv_end = causal ? (N < (qt + 1) * BR ? N : (qt + 1) * BR) : N;
@@ -58,27 +62,30 @@ static void fwd128(int N, bool causal) {
     for (int t = 0; t < nkv; ++t) {
       const int key0 = t * BC, slot = t & (SLOTS - 1);
       const bool full = key0 + BC <= N;
-      std::vector<int> hits(2 * TILEB / 16, 0);
+      std::vector<int> hits(TILEB / 16, 0);
       for (int wave = 0; wave < 8; ++wave)
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NLD; ++i)
           for (int lane = 0; lane < 64; ++lane) {
-            const int r = fwd128_row(wave, lane, i);
+            const int r = fwd_row<D>(wave, lane, i);
             const uint32_t back = full ? 0u : back_of(key0, r, N, ROWB);
             const int row = key0 + r < N - 1 ? key0 + r : N - 1;
             const int64_t base = (int64_t)key0 * ROWB;
-            check_load("fwd128 K", N, 128, ROWB, base, fwd128_k_off(wave, lane, i), back, row,
-                       (lane & 15) ^ (r & 15), t, wave, lane);
-            check_load("fwd128 V", N, 128, ROWB, base, fwd128_v_off(wave, lane, i), back, row,
-                       (lane & 15) ^ ((r & 3) << 2), t, wave, lane);
-            const int dk = slot * TILEB + (2 * wave + i) * 1024 + 16 * lane;   // K ring; V at +VREGION
+            const int c = lane % CPR;
+            const int kc = D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+            const int vc = D == 128 ? c ^ ((r & 3) << 2) : c ^ (((r >> 1) & 1) << 2);
+            check_load(D == 128 ? "fwd128 K" : "fwd64 K", N, D, ROWB, base, fwd_k_off<D>(wave, lane, i), back, row, kc,
+                       t, wave, lane);
+            check_load(D == 128 ? "fwd128 V" : "fwd64 V", N, D, ROWB, base, fwd_v_off<D>(wave, lane, i), back, row, vc,
+                       t, wave, lane);
+            const int dk = slot * TILEB + (NLD * wave + i) * 1024 + 16 * lane;   // K ring; V at +VREGION
             if (dk < slot * TILEB || dk + 16 > (slot + 1) * TILEB || dk + VREGION + 16 > LDS)
-              bad("LDS write outside the slot", "fwd128", N, 128, t, wave, lane, dk);
-            if ((dk - slot * TILEB) / ROWB != r || ((dk - slot * TILEB) % ROWB) / 16 != (lane & 15))
-              bad("LDS place is not the loaded row's physical chunk", "fwd128", N, 128, t, wave, lane, dk);
+              bad("LDS write outside the slot", kn, N, D, t, wave, lane, dk);
+            if ((dk - slot * TILEB) / ROWB != r || ((dk - slot * TILEB) % ROWB) / 16 != c)
+              bad("LDS place is not the loaded row's physical chunk", kn, N, D, t, wave, lane, dk);
             ++hits[(dk - slot * TILEB) / 16];
           }
       for (int p = 0; p < TILEB / 16; ++p)
-        if (hits[p] != 1) bad("tile place not written exactly once", "fwd128", N, 128, t, p, 0, hits[p]);
+        if (hits[p] != 1) bad("tile place not written exactly once", kn, N, D, t, p, 0, hits[p]);
     }
   }
 }
@@ -169,7 +176,8 @@ int main(int argc, char** argv) {
   for (int N : Ns) {
     if (N < 1) continue;
     for (int causal = 0; causal < 2; ++causal) {
-      fwd128(N, causal);
+      fwd<128>(N, causal);
+      fwd<64>(N, causal);
       dq<64>(N, causal);
       dq<128>(N, causal);
       if (N <= 8192) {   // (the dK/dV walk is quadratic in N; it is covered up to 8192)

@@ -59,39 +59,42 @@ def test_causal_medium_full(causal):
     full_parity(t, "bf16", 1 / math.sqrt(128), causal, f"n777 causal={causal}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d,H", [(64, 2), (64, 86), (128, 2)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_late_keys_far_above_the_running_max(d, causal):
+def test_late_keys_far_above_the_running_max(d, H, causal):
     """Keys whose logits lie far above every earlier score arrive in later tiles (a raise of
     the exponent reference after the first tile, twice, the second by 100 in natural units):
     every query that sees them puts its weight there. Logit offsets come from a constant last
-    query coordinate, as in the boosted-key workload."""
+    query coordinate, as in the boosted-key workload. d = 64 runs the generic kernel on 2 heads
+    and the tuned one on 86 (258 tiles of 256 queries); d = 128 always runs the tuned one."""
     N, scale = 700, 1.0 / math.sqrt(d)
-    t = inputs.make_random(1, 2, N, d, "bf16", seed=77)
+    t = inputs.make_random(1, H, N, d, "bf16", seed=77)
     q, k = t["q"].copy(), t["k"].copy()
     q[..., d - 1] = inputs.f32_to_bf16_bits(np.float32(1.0))
     k[..., d - 1] = 0
     for key, logit in ((210, 50.0), (610, 100.0)):
         k[:, :, key, d - 1] = inputs.f32_to_bf16_bits(np.float32(logit / scale))
     t = {"q": q, "k": k, "v": t["v"]}
-    full_parity(t, "bf16", scale, causal, f"late spikes d{d} causal={causal}")
+    full_parity(t, "bf16", scale, causal, f"late spikes d{d} H{H} causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("gap", [30.0, 40.0])
-def test_large_gap_without_a_raise(gap, causal):
-    """d = 128 (the tuned kernel): a key 30 or 40 natural units above every score of the first
-    tiles arrives in a later tile. The tuned kernel raises its exponent reference only when a
-    tile's per-lane sum passes 2^64, so probabilities of about e^30 = 2^43 and e^40 = 2^58 flow
-    through the bf16 probabilities and the fp32 denominator and numerator without a raise."""
-    N, d, scale = 700, 128, 1.0 / math.sqrt(128)
-    t = inputs.make_random(1, 2, N, d, "bf16", seed=78)
+@pytest.mark.parametrize("d,H", [(128, 2), (64, 86)])
+def test_large_gap_without_a_raise(d, H, gap, causal):
+    """The tuned kernel (d = 128; d = 64 on 86 heads, 258 tiles of 256 queries): a key 30 or 40
+    natural units above every score of the first tiles arrives in a later tile. The tuned kernel
+    raises its exponent reference only when a tile's per-lane sum passes 2^64, so probabilities
+    of about e^30 = 2^43 and e^40 = 2^58 flow through the bf16 probabilities and the fp32
+    denominator and numerator without a raise."""
+    N, scale = 700, 1.0 / math.sqrt(d)
+    t = inputs.make_random(1, H, N, d, "bf16", seed=78)
     q, k = t["q"].copy(), t["k"].copy()
     q[..., d - 1] = inputs.f32_to_bf16_bits(np.float32(1.0))
     k[..., d - 1] = 0
     k[:, :, 333, d - 1] = inputs.f32_to_bf16_bits(np.float32(gap / scale))
     t = {"q": q, "k": k, "v": t["v"]}
-    full_parity(t, "bf16", scale, causal, f"gap {gap} without a raise, causal={causal}")
+    full_parity(t, "bf16", scale, causal, f"gap {gap} without a raise, d{d} H{H} causal={causal}")
 
 
 def _sweep_case(i: int):
@@ -225,12 +228,13 @@ def test_other_scales(dtype, scale):
         full_parity(t, dtype, scale, causal, f"{dtype} scale={scale} causal={causal}", tol)
 
 
-@pytest.mark.parametrize("B,H,N,d", [(4, 64, 256, 64), (2, 64, 300, 48), (1, 128, 513, 64), (2, 64, 257, 17)])
+@pytest.mark.parametrize("B,H,N,d", [(2, 64, 200, 64), (2, 64, 300, 48), (1, 128, 250, 64), (2, 64, 257, 17)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_d64_wide_blocks(B, H, N, d, causal):
     """Grids of at least 256 workgroups of 128 queries run the 4-wave blocks at head widths up
-    to 64 (many heads; ragged query and key tails, partial head widths, two to five query
-    tiles per head)."""
+    to 64 (many heads; ragged query and key tails, partial head widths, two or three query
+    tiles per head). At width exactly 64 these grids stay below 256 tiles of 256 queries, where
+    the tuned kernel would take over."""
     t = inputs.make_random(B, H, N, d, "bf16", seed=1400 + N + d + H)
     full_parity(t, "bf16", 1 / math.sqrt(d), causal, f"bf16 wide B{B} H{H} N{N} d{d} causal={causal}")
 
@@ -238,21 +242,33 @@ def test_bf16_d64_wide_blocks(B, H, N, d, causal):
 @pytest.mark.parametrize("name", ["sweep_bf16_b1_h16_n8192_d32", "sweep_bf16_b1_h16_n8192_d64",
                                   "sweep_bf16_b1_h16_n8192_d96", "sweep_bf16_b1_h16_n8192_d256"])
 def test_head_width_sweep_sampled_rows(name):
-    """The other head widths at the headline's B, H and N (the 4-wave blocks at widths up to 64,
-    the generic 128- and 256-wide blocks above), on sampled rows of every head."""
+    """The other head widths at the headline's B, H and N (the 4-wave blocks at width 32, the
+    tuned two-group kernel at exactly 64, the generic 128- and 256-wide blocks above), on
+    sampled rows of every head."""
     sampled_parity(inputs.ALL_WORKLOADS[name], 32, name)
 
 
+@pytest.mark.parametrize("B,H,N", [(4, 64, 256), (1, 128, 513)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_d64_tuned(B, H, N, causal):
+    """Width exactly 64 with at least 256 tiles of 256 queries runs the tuned two-group kernel
+    (one key-row swizzle and DMA map per width): every output compared, a whole tile per head
+    and a ragged one."""
+    t = inputs.make_random(B, H, N, 64, "bf16", seed=1500 + N + H)
+    full_parity(t, "bf16", 1 / 8, causal, f"bf16 tuned d64 B{B} H{H} N{N} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("B,H,N", [(3, 40, 600), (2, 100, 300), (1, 130, 1000)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_d128_more_items_than_cus(B, H, N, causal):
-    """d = 128 grids with more (query tile, head) items than CUs, where each workgroup stays
-    resident and runs a sequence of items; ragged N, so items of different lengths and ragged
-    last tiles follow each other in one workgroup. Oracle on sampled rows of every head."""
-    d = 128
+def test_tuned_more_items_than_cus(d, B, H, N, causal):
+    """Tuned-kernel grids (d = 128, and d = 64 at these sizes) with more (query tile, head)
+    items than CUs, where each workgroup stays resident and runs a sequence of items; ragged N,
+    so items of different lengths and ragged last tiles follow each other in one workgroup.
+    Oracle on sampled rows of every head."""
     label = f"bf16 B{B} H{H} N{N} d{d} causal={causal} ({B * H * -(-N // 256)} items)"
     note(f"resident workgroups {label}")
-    t = inputs.make_random(B, H, N, d, "bf16", seed=7000 + B * 100 + H + N)
+    t = inputs.make_random(B, H, N, d, "bf16", seed=7000 + B * 100 + H + N + d)
     scale = 1 / math.sqrt(d)
     o, l = run_gpu(t, "bf16", scale, causal)
     rows = np.stack([np.stack([inputs.sample_rows(N, 16, seed=B * H * 10 + b * H + h)[:16] for h in range(H)])
