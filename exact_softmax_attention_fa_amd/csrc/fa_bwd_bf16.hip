@@ -107,12 +107,14 @@ __device__ __forceinline__ u32x4 read_tr(const uint16_t* tile, int c16, const Ti
 // One 16-byte-per-lane (or 4-byte-per-lane) global -> LDS load: lane l's data lands at LDS
 // byte lds_addr + 16 l (+ 4 l). Issued through inline assembly so that the compiler's wait
 // insertion does not tie later LDS reads to it; completion is tracked by hand (step_barrier).
+// An LDS DMA needs a wait state after the scalar write of M0 that gives its LDS address (the
+// s_nop).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
 }
 

@@ -267,12 +267,16 @@ __device__ __forceinline__ void tile_step(const uint16_t* __restrict__ Ks, const
       l_run[qb] *= alpha;
       // In-place multiply: tying each output to its input register keeps the compiler from
       // copying the whole accumulator to merge the taken and not-taken paths. (The 256-wide
-      // accumulators live in AGPRs, which the VGPR constraint would force out of them.)
+      // accumulators live in AGPRs, which the VGPR constraint would force out of them.) The
+      // compiler does not count inline asm as a reader of a transcendental result, which needs a
+      // wait state after the v_exp_f32 that may write it; the s_nop in front provides it.
+      float alpha_r = alpha;
+      if constexpr (D <= 128) asm volatile("s_nop 1" : "+v"(alpha_r));
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          if constexpr (D <= 128) asm("v_mul_f32 %0, %0, %1" : "+v"(acc[qb][dt][i]) : "v"(alpha));
+          if constexpr (D <= 128) asm("v_mul_f32 %0, %0, %1" : "+v"(acc[qb][dt][i]) : "v"(alpha_r));
           else acc[qb][dt][i] *= alpha;
         }
       m_run[qb] = m_new;

@@ -95,6 +95,15 @@ __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// A VALU instruction that reads the result of a transcendental one (v_exp_f32) needs a wait
+// state between them. The compiler provides it for the instructions it emits, but it does not
+// treat inline asm as a reader, so a value that inline asm will read right after a v_exp_f32
+// passes through an s_nop first (two wait states; the raise path only).
+__device__ __forceinline__ float asm_ready(float x) {
+  asm volatile("s_nop 1" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 x = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
@@ -104,9 +113,10 @@ template <int V> struct IntC { static constexpr int value = V; };
 
 // One 16-byte-per-lane global -> LDS load: lane l's data lands at LDS byte lds_addr + 16*l.
 // Issued through inline assembly so that the compiler's wait insertion does not treat every
-// later LDS read as dependent on it; completion is tracked by hand (phase_barrier).
+// later LDS read as dependent on it; completion is tracked by hand (phase_barrier). An LDS DMA
+// needs a wait state after the scalar write of M0 that gives its LDS address (the s_nop).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory");
 }
 
@@ -440,10 +450,13 @@ __device__ __forceinline__ void fwd_tuned_body(FwdArgs a, int causal_flag) {
       const float m_new = fmaxf(m_run, pair_max(fmaxf(m0, m1) * a.sl2));
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
+      // In-place multiplies (inline asm, so that the compiler keeps one copy of the accumulator
+      // across the branch) of a value that v_exp_f32 has just written: see asm_ready.
+      const float alpha_r = asm_ready(alpha);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) asm("v_mul_f32 %0, %0, %1" : "+v"(acc[dt][i]) : "v"(alpha));
+        for (int i = 0; i < 16; ++i) asm("v_mul_f32 %0, %0, %1" : "+v"(acc[dt][i]) : "v"(alpha_r));
       m_run = m_new;
       exps();
     }
