@@ -6,9 +6,13 @@
 // written exactly once. The loop structure (which tiles each kernel issues for a given N and
 // mask) restates the kernels' own.
 //
-// usage: dma_bounds [--old-dq-base | --no-back] N1 N2 ...
+// It also walks the forward ring schedule (which interval requests, reads and reuses each
+// slot) for every tile count the lengths give.
+//
+// usage: dma_bounds [--old-dq-base | --no-back | --deep-lead] N1 N2 ...
 //   --old-dq-base  plants the dQ kernel's earlier base row (not clamped to N-1)
 //   --no-back      plants loads that never pull rows past N-1 back
+//   --deep-lead    plants a forward ring lead one tile deeper than the ring allows
 // Prints the counts and the first violations; exit status 1 if any load violates a check.
 #include <stdint.h>
 #include <stdio.h>
@@ -21,7 +25,7 @@
 
 using namespace fa::dma;
 
-static bool g_old_dq = false, g_no_back = false;
+static bool g_old_dq = false, g_no_back = false, g_deep_lead = false;
 static long g_loads = 0, g_bad = 0;
 
 static void bad(const char* what, const char* kernel, int N, int D, int a, int b, int c, long long v) {
@@ -54,13 +58,14 @@ template <int D>
 static void fwd(int N, bool causal) {
   const int BR = 256, BC = 64, SLOTS = 4, ROWB = fwd_row_bytes<D>(), TILEB = BC * ROWB;
   const int VREGION = SLOTS * TILEB, LDS = 2 * SLOTS * TILEB, CPR = D / 8, NLD = D / 64;
+  if (LDS > 160 * 1024) bad("rings exceed the CU's LDS", "fwd", N, D, 0, 0, 0, LDS);
   const char* kn = D == 128 ? "fwd128" : "fwd64";
   const int nqt = (N + BR - 1) / BR;
   for (int qt = 0; qt < nqt; ++qt) {
     const int kv_end = causal ? (N < (qt + 1) * BR ? N : (qt + 1) * BR) : N;
     const int nkv = (kv_end + BC - 1) / BC;
     for (int t = 0; t < nkv; ++t) {
-      const int key0 = t * BC, slot = t & (SLOTS - 1);
+      const int key0 = t * BC, slot = t % SLOTS;
       const bool full = key0 + BC <= N;
       std::vector<int> hits(TILEB / 16, 0);
       for (int wave = 0; wave < 8; ++wave)
@@ -86,6 +91,55 @@ static void fwd(int N, bool causal) {
           }
       for (int p = 0; p < TILEB / 16; ++p)
         if (hits[p] != 1) bad("tile place not written exactly once", kn, N, D, t, p, 0, hits[p]);
+    }
+  }
+}
+
+// ---- forward, tuned kernels: the ring schedule ------------------------------------------------
+// Restated from the phase definitions: group g runs M_j in interval 2j+g and V_j in 2j+1+g
+// (j < nkv), and the final M_nkv in 2nkv+g. M_j reads K_j (j < nkv) and V_{j-1}; the end of V_j
+// requests V_j operands for M_{j+1}. Group g requests tiles 0 .. lead_g-1 before interval 0 and
+// tile j+lead_g at the start of V_j (lead = S-2, S-1), into slot t mod S. The barrier closing
+// interval k waits until at most `ahead` of the wave's newest tiles are in flight, with
+// ahead = (last tile requested) - (k+1)/2 and at most 4 supported. Checks: every slot is
+// rewritten only after every read of its previous tile; every tile is requested by both groups
+// before the barrier that closes the interval before its first read, and that barrier waits for
+// it; the in-flight count never exceeds 4.
+static void fwd_schedule(int nkv, int S) {
+  const char* kn = "fwd ring";
+  std::vector<int> last_read(nkv, -1), first_read(nkv, 1 << 30);
+  auto read = [&](int t, int k) {
+    if (t < 0 || t >= nkv) return;
+    last_read[t] = k > last_read[t] ? k : last_read[t];
+    first_read[t] = k < first_read[t] ? k : first_read[t];
+  };
+  for (int g = 0; g < 2; ++g)
+    for (int j = 0; j <= nkv; ++j) {
+      const int km = 2 * j + g;
+      if (j < nkv) read(j, km);    // K_j in M_j
+      read(j - 1, km);             // V_{j-1} in M_j
+      if (j < nkv) read(j, km + 1);   // V_j operand requests at the end of V_j
+    }
+  for (int g = 0; g < 2; ++g) {
+    const int lead = (g == 0 ? S - 2 : S - 1) + (g_deep_lead ? 1 : 0);
+    std::vector<int> issue(nkv, 0);   // interval at whose start the group requests tile t (-1: prologue)
+    for (int t = 0; t < nkv; ++t) issue[t] = t < lead ? -1 : 2 * (t - lead) + 1 + g;
+    for (int t = 0; t < nkv; ++t) {
+      if (t >= S && issue[t] <= last_read[t - S])
+        bad("slot rewritten before its last read", kn, nkv, S, t, g, issue[t], last_read[t - S]);
+      // the barrier closing interval first_read-1 waits for tiles up to first_read/2
+      if (first_read[t] < 2 * t) bad("tile read before a barrier waits for it", kn, nkv, S, t, g, first_read[t], 0);
+      if (issue[t] > first_read[t] - 1)
+        bad("tile requested after the barrier before its first read", kn, nkv, S, t, g, issue[t], first_read[t]);
+    }
+    // both groups close intervals 0 .. 2nkv with a barrier (group 1: an extra one first, none
+    // after its final M phase); requests at the start of interval k count at its barrier
+    for (int k = 0; k <= 2 * nkv; ++k) {
+      int last = -1;
+      for (int t = 0; t < nkv; ++t)
+        if (issue[t] <= k) last = t;
+      const int ahead = last - ((k + 1) >> 1);
+      if (ahead > 4) bad("more tiles in flight than the barrier waits for", kn, nkv, S, k, g, ahead, 0);
     }
   }
 }
@@ -171,6 +225,7 @@ int main(int argc, char** argv) {
   for (int a = 1; a < argc; ++a) {
     if (!strcmp(argv[a], "--old-dq-base")) g_old_dq = true;
     else if (!strcmp(argv[a], "--no-back")) g_no_back = true;
+    else if (!strcmp(argv[a], "--deep-lead")) g_deep_lead = true;
     else Ns.push_back(atoi(argv[a]));
   }
   for (int N : Ns) {
@@ -178,6 +233,8 @@ int main(int argc, char** argv) {
     for (int causal = 0; causal < 2; ++causal) {
       fwd<128>(N, causal);
       fwd<64>(N, causal);
+      const int nkv = (N + 63) / 64;   // key tiles of the longest item (whole N)
+      for (int S = 4; S <= 6; ++S) fwd_schedule(nkv, S);
       dq<64>(N, causal);
       dq<128>(N, causal);
       if (N <= 8192) {   // (the dK/dV walk is quadratic in N; it is covered up to 8192)

@@ -1,10 +1,12 @@
-"""The address arithmetic of the direct global -> LDS tile loads (fa_dma.h, used by the d = 128
-forward kernel and both backward kernels), walked on the host for every load of every wave:
+"""The address arithmetic of the direct global -> LDS tile loads (fa_dma.h, used by the tuned
+forward kernels, d = 128 and 64, and both backward kernels), walked on the host for every load of every wave:
 N = 1..600 and the workloads' lengths, both masks, head widths 64 and 128. Each load must read
 inside its head, read the row and chunk it should, write inside its LDS slot, and cover every
-place of its tile once. Two planted mistakes must be caught: the dQ kernel's earlier base row
-(not clamped to N-1, which made the unsigned lane offsets wrap for N < 64) and loads that do not
-pull rows past N-1 back."""
+place of its tile once. The forward kernels' ring schedule is walked as well (which phase
+interval requests, reads and reuses each slot, for rings of 4 to 6 slots). Three planted mistakes
+must be caught: the dQ kernel's earlier base row (not clamped to N-1, which made the unsigned
+lane offsets wrap for N < 64), loads that do not pull rows past N-1 back, and a ring lead one
+tile deeper than the slots allow."""
 import os
 import shutil
 import subprocess
@@ -46,3 +48,8 @@ def test_unclamped_dq_base_is_caught(checker):
 def test_missing_pull_back_is_caught(checker):
     r = run(checker, "--no-back", "1", "31", "65", "100", "300")
     assert r.returncode == 1 and "read outside the head" in r.stderr
+
+
+def test_too_deep_ring_lead_is_caught(checker):
+    r = run(checker, "--deep-lead", "64", "300", "1000")
+    assert r.returncode == 1 and "slot rewritten before its last read" in r.stderr
