@@ -72,6 +72,18 @@ def fp32_scaled_tolerance(d: int, scale: float) -> dict:
     return {"max": 1e-5 * f, "mean": 1e-5 * f, "lse": 1e-3}
 
 
+def bf16_peaky_tolerance(v_bits: np.ndarray) -> dict:
+    """bf16 tolerance for logits larger than the workloads'. With peaky weights an output row is
+    close to a single value row, so |o| approaches max|v|. A bf16 rounding (7 stored mantissa
+    bits, round to nearest) moves x by at most 2^-8 |x|; the kernel rounds the probabilities
+    (error at most 2^-8 sum p|v| / l <= 2^-8 max|v|) and its output, and the stored reference
+    output is rounded once more, so the two outputs differ by at most 3 * 2^-8 * max|v| plus fp32
+    terms far below it. The workload bound 0.02 stays the floor; mean and lse bounds are kept."""
+    v = (np.asarray(v_bits).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    vmax = float(np.abs(v).max())
+    return {"max": max(TOL["bf16"]["max"], 3 * 2.0 ** -8 * vmax), "mean": TOL["bf16"]["mean"], "lse": TOL["bf16"]["lse"]}
+
+
 def sampled_parity(w: inputs.Workload, rows_per_head: int, label: str):
     """Full-size workload on the GPU, oracle on sampled query rows of every (b, h)."""
     note(f"sampled parity {label}: {w.name}")

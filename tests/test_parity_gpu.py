@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from exact_softmax_attention_fa_amd import inputs
-from gpu_util import compare, fp32_scaled_tolerance, full_parity, note, run_gpu, sampled_parity
+from gpu_util import bf16_peaky_tolerance, compare, fp32_scaled_tolerance, full_parity, note, run_gpu, sampled_parity
 from oracle import attention as oracle
 
 pytestmark = pytest.mark.gpu
@@ -250,12 +250,16 @@ def test_head_width_sweep_sampled_rows(name):
 
 @pytest.mark.parametrize("B,H,N", [(4, 64, 256), (1, 128, 513)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bf16_d64_tuned(B, H, N, causal):
+@pytest.mark.parametrize("scale", [1 / 8, -0.3, 0.0, 2.5])
+def test_bf16_d64_tuned(B, H, N, causal, scale):
     """Width exactly 64 with at least 256 tiles of 256 queries runs the tuned two-group kernel
-    (one key-row swizzle and DMA map per width): every output compared, a whole tile per head
-    and a ragged one."""
+    (its own key-row swizzle and DMA map): every output compared, a whole tile per head and a
+    ragged one, at the workload scale and at negative, zero and large scales (2.5: logits 20x
+    the workload's, so the reference is raised often). Above the workload scale the output
+    bound is the one for peaky weights, 3 * 2^-8 * max|v| (bf16_peaky_tolerance)."""
     t = inputs.make_random(B, H, N, 64, "bf16", seed=1500 + N + H)
-    full_parity(t, "bf16", 1 / 8, causal, f"bf16 tuned d64 B{B} H{H} N{N} causal={causal}")
+    tol = bf16_peaky_tolerance(t["v"]) if abs(scale) * 8 > 1 else None
+    full_parity(t, "bf16", scale, causal, f"bf16 tuned d64 B{B} H{H} N{N} scale={scale} causal={causal}", tol)
 
 
 @pytest.mark.parametrize("d", [128, 64])
