@@ -580,7 +580,13 @@ hipError_t launch_tuned(const FwdArgs& a, bool causal, hipStream_t stream) {
 
 int bf16_tuned_rows_per_block() { return BR; }
 
-bool bf16_tuned_d64(int64_t BH, int N) { return BH * (((int64_t)N + BR - 1) / BR) >= 256; }
+// Head width 64 runs the tuned kernel when the grid has at least one tile of 256 queries per CU;
+// smaller grids keep the generic blocks (more, smaller workgroups). FA_TUNED_D64=0 (a timing
+// build) sends every width-64 call to the generic blocks.
+#ifndef FA_TUNED_D64
+#define FA_TUNED_D64 1
+#endif
+bool bf16_tuned_d64(int64_t BH, int N) { return FA_TUNED_D64 && BH * (((int64_t)N + BR - 1) / BR) >= 256; }
 
 hipError_t launch_bf16_tuned(const FwdArgs& a, bool causal, hipStream_t stream) {
   return a.d == 128 ? launch_tuned<128>(a, causal, stream) : launch_tuned<64>(a, causal, stream);
