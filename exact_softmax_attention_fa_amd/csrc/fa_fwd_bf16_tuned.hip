@@ -8,7 +8,8 @@
 // * 8 waves per workgroup, 32 query rows each (256 rows per workgroup), two waves per SIMD.
 //   The waves form two groups (waves 0-3 and 4-7, one wave of each group per SIMD) that run
 //   one phase apart. Every key tile j is handled in two phases per wave:
-//     M_j: O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs), then S_j^T = K_j Q^T (16 MFMAs)
+//     M_j: O^T += V_{j-1}^T P_{j-1}^T, then S_j^T = K_j Q^T (D/8 MFMAs each: 16 at D = 128,
+//          8 at D = 64)
 //     V_j: online-softmax update of S_j into P_j (exponentials and the other VALU work)
 //   separated by workgroup barriers. While one group is in an M phase the other is in a V
 //   phase, so each SIMD keeps its matrix unit busy with one wave while the other wave's
@@ -41,8 +42,9 @@
 // * The output rows leave through LDS (the K ring is idle after the last barrier of an item),
 //   so that every store writes whole rows.
 // * When there are more work items (query tile, head) than workgroups that fit on the chip at
-//   once, that many stay resident and each runs a fixed sequence of items: no dispatch gap between items, and under the
-//   causal mask a balanced total per workgroup (see the schedule below).
+//   once, that many stay resident and each runs a fixed sequence of items: no dispatch gap
+//   between items, and under the causal mask a balanced total per workgroup (see the schedule
+//   below).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -323,8 +325,8 @@ __device__ __forceinline__ void fwd_tuned_body(FwdArgs a, int causal_flag) {
 #endif
   constexpr int PF = FA_PF;     // K operand steps in flight
   constexpr int PFV = FA_PFV;   // V operand steps in flight (requested in the V phase before)
-  constexpr int S_STEPS = D / 16;                  // S^T = K Q^T: 8 steps of two MFMAs
-  constexpr int PV_STEPS = (BC / 16) * (D / 32);   // O^T += V^T P^T: 16 MFMAs
+  constexpr int S_STEPS = D / 16;                  // S^T = K Q^T: steps of two MFMAs
+  constexpr int PV_STEPS = (BC / 16) * (D / 32);   // O^T += V^T P^T: one MFMA per step
   u32x4 kb0[S_STEPS], kb1[S_STEPS];   // K operands of the two 32-key blocks
   u32x4 av[PV_STEPS];                 // V^T operands
   auto k_load = [&](int kk, auto ks_tag) __attribute__((always_inline)) {
