@@ -265,6 +265,17 @@ def test_bf16_d64_tuned(B, H, N, causal, scale):
     full_parity(t, "bf16", scale, causal, f"bf16 tuned d64 B{B} H{H} N{N} scale={scale} causal={causal}", tol)
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 256, 1), (1, 256, 33), (2, 128, 65), (1, 256, 130), (2, 128, 255),
+                                   (1, 300, 65)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_d64_tuned_short(B, H, N, causal):
+    """The tuned d = 64 kernel on short sequences over at least 256 heads: items of one or two key
+    tiles (N = 1, 33, 65, 130, 255), a ragged first tile, the final-phase slot for those tile
+    counts, and (300 heads) resident workgroups running a second short item."""
+    t = inputs.make_random(B, H, N, 64, "bf16", seed=1700 + N + H)
+    full_parity(t, "bf16", 1 / 8, causal, f"bf16 tuned d64 short B{B} H{H} N{N} causal={causal}")
+
+
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("B,H,N", [(3, 40, 600), (2, 100, 300), (1, 130, 1000)])
 @pytest.mark.parametrize("causal", [False, True])
