@@ -313,15 +313,16 @@ __device__ __forceinline__ void fwd_tuned_body(FwdArgs a, int causal_flag) {
   if (grp == 1 && nkv > 2) issue_tile(2);
   phase_barrier<LOADS_PER_TILE>(last_issued);
 
-  // Operand reads run PF steps ahead of the MFMAs; scheduling barriers keep the compiler from
-  // sinking them next to their uses. The reads of one product's first PF steps are issued
-  // before it starts, in the preceding phase or product, so that no product waits for LDS at
-  // its start.
+  // Operand reads run PF (K) and PFV (V) steps ahead of the MFMAs; scheduling barriers keep the
+  // compiler from sinking them next to their uses. The reads of one product's first steps are
+  // issued before it starts, in the preceding phase or product, so that no product waits for
+  // LDS at its start. Shallow depths measured best (2 and 1: fewer reads in the softmax phase,
+  // which is as critical as the matrix phase; deeper ones were up to 3% slower).
 #ifndef FA_PF
-#define FA_PF 3
+#define FA_PF 2
 #endif
 #ifndef FA_PFV
-#define FA_PFV 3
+#define FA_PFV 1
 #endif
   constexpr int PF = FA_PF;     // K operand steps in flight
   constexpr int PFV = FA_PFV;   // V operand steps in flight (requested in the V phase before)
