@@ -40,11 +40,12 @@ CSRC = "exact_softmax_attention_fa_amd/csrc/"
 
 def kernel_sources(w: inputs.Workload) -> list:
     """Sources of the kernel a workload runs (the key under which its traffic is stored): the
-    kernel, the headers it includes and the front end that computes its launch arguments."""
+    kernel, the headers it includes and the front end that computes its launch arguments (for
+    the tuned kernels also the bf16 dispatcher that routes widths 64 and 128 to them)."""
     if w.dtype == "f32":
         main = ["fa_fwd_f32.hip"]
     elif w.d == 128 or (w.d == 64 and w.B * w.H * -(-w.N // 256) >= 256):   # the tuned kernels
-        main = ["fa_fwd_bf16_tuned.hip", "fa_dma.h"]
+        main = ["fa_fwd_bf16_tuned.hip", "fa_dma.h", "fa_fwd_bf16.hip"]
     else:
         main = ["fa_fwd_bf16.hip"]
     return [CSRC + m for m in main + ["fa_internal.h", "fa_api.hip"]]

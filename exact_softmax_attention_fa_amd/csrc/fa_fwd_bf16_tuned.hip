@@ -328,6 +328,7 @@ __device__ __forceinline__ void fwd_tuned_body(FwdArgs a, int causal_flag) {
   constexpr int PFV = FA_PFV;   // V operand steps in flight (requested in the V phase before)
   constexpr int S_STEPS = D / 16;                  // S^T = K Q^T: steps of two MFMAs
   constexpr int PV_STEPS = (BC / 16) * (D / 32);   // O^T += V^T P^T: one MFMA per step
+  static_assert(PF >= 1 && PF <= S_STEPS && PFV >= 1 && PFV <= PV_STEPS, "prefetch depth within a product");
   u32x4 kb0[S_STEPS], kb1[S_STEPS];   // K operands of the two 32-key blocks
   u32x4 av[PV_STEPS];                 // V^T operands
   auto k_load = [&](int kk, auto ks_tag) __attribute__((always_inline)) {
